@@ -1,0 +1,94 @@
+"""Acceptance check of a GPU result against the oracle -- TEST INFRASTRUCTURE ONLY.
+
+The bound is the one the GEMM is accepted under (fp32 accumulation of exact bf16 products):
+
+    fp32 output:  |C - C_ref| <= t1,            t1 = 4 * K * 2^-24 * (|A| |B|^T)
+    bf16 output:  |C - C_ref| <= t1 + 2^-8 * (|C_ref| + t1)
+
+The extra bf16 term is the unit roundoff of an 8-bit significand (round to nearest) taken
+relative to the magnitude of the fp32 result, which is at most |C_ref| + t1; this keeps the
+allowance meaningful where C_ref cancels to ~0.  Any NaN or Inf in C fails.
+
+Where every partial sum is an integer below 2^24 (integer-valued inputs), fp32 accumulation
+is exact in any order, so there the check is bitwise: ``check_exact``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+OUT_FP32 = 0
+OUT_BF16 = 1
+
+
+def bf16_bits_to_f64(h: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float64 for comparison."""
+    h = np.asarray(h, dtype=np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bound(C_ref: np.ndarray, Mag: np.ndarray, K: int, out_dtype: int) -> np.ndarray:
+    t1 = 4.0 * K * 2.0 ** -24 * Mag
+    if out_dtype == OUT_FP32:
+        return t1
+    if out_dtype == OUT_BF16:
+        return t1 + 2.0 ** -8 * (np.abs(C_ref) + t1)
+    raise ValueError(f"unknown out_dtype {out_dtype}")
+
+
+def to_f64(C, out_dtype: int) -> np.ndarray:
+    """GPU output (float32 array, or uint16 bf16 bit patterns) -> float64."""
+    C = np.asarray(C)
+    if out_dtype == OUT_BF16:
+        if C.dtype != np.uint16:
+            raise TypeError("bf16 output must be given as uint16 bit patterns")
+        return bf16_bits_to_f64(C)
+    if C.dtype != np.float32:
+        raise TypeError("fp32 output must be given as float32")
+    return C.astype(np.float64)
+
+
+def check(C, C_ref: np.ndarray, Mag: np.ndarray, K: int, out_dtype: int) -> dict:
+    """Elementwise bound check.  Returns a summary dict; ``ok`` is the verdict."""
+    Cg = to_f64(C, out_dtype)
+    if Cg.shape != C_ref.shape:
+        raise ValueError(f"shape mismatch {Cg.shape} vs {C_ref.shape}")
+    b = bound(C_ref, Mag, K, out_dtype)
+    err = np.abs(Cg - C_ref)
+    finite = np.isfinite(Cg)
+    bad = ~finite | (err > b)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(b > 0, err / np.where(b > 0, b, 1.0), np.where(err > 0, np.inf, 0.0))
+    ratio = np.where(finite, ratio, np.inf)
+    return {
+        "ok": bool(not bad.any()),
+        "n": int(Cg.size),
+        "n_fail": int(bad.sum()),
+        "n_nonfinite": int((~finite).sum()),
+        "max_err_over_bound": float(ratio.max()) if ratio.size else 0.0,
+        "max_abs_err": float(err[finite].max()) if finite.any() else 0.0,
+    }
+
+
+def check_exact(C, expected, out_dtype: int) -> dict:
+    """Bitwise comparison: float32 values for fp32 output, bit patterns for bf16 output."""
+    C = np.asarray(C)
+    expected = np.asarray(expected)
+    if out_dtype == OUT_FP32:
+        a = C.astype(np.float32).view(np.uint32)
+        e = expected.astype(np.float32).view(np.uint32)
+        # +0 and -0 are the same sum
+        a = np.where(a == 0x80000000, 0, a)
+        e = np.where(e == 0x80000000, 0, e)
+    else:
+        a = C.astype(np.uint16)
+        e = expected.astype(np.uint16)
+        a = np.where(a == 0x8000, 0, a)
+        e = np.where(e == 0x8000, 0, e)
+    diff = a != e
+    idx = np.argwhere(diff)
+    return {
+        "ok": bool(not diff.any()),
+        "n": int(a.size),
+        "n_fail": int(diff.sum()),
+        "first_fail": tuple(int(v) for v in idx[0]) if idx.size else None,
+    }

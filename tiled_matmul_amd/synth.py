@@ -1,0 +1,211 @@
+"""Seeded synthetic inputs for the bf16 GEMM, shared by the tests, the bench and the oracle's
+callers.  This module holds none of the GEMM's arithmetic: it only draws numbers and rounds
+them to bf16 bit patterns (uint16 arrays), which are then handed unchanged to both the GPU
+path and the CPU oracle.
+
+Generator.  SplitMix64 (G. L. Steele, D. Lea, C. H. Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014), used counter-based: the draw with counter c under seed s
+is mix64(key(s) + (c + 1) * 0x9E3779B97F4A7C15) with key(s) = mix64(s), so any element can
+be regenerated on its own.  Element (r, c) of a rows x cols operand uses counter r*cols + c
+(independent of the row pitch).
+
+Distributions:
+  uniform [lo, hi):  u = (z >> 40) * 2^-24 in [0, 1);  lo + (hi - lo) * u
+  normal (0, s^2):   Box-Muller from the draws 2e and 2e+1 of element e:
+                     u1 = ((z1 >> 11) + 1) * 2^-53 in (0, 1], u2 = (z2 >> 11) * 2^-53,
+                     s * sqrt(-2 ln u1) * cos(2 pi u2)
+  integer [lo, hi]:  lo + (z >> 32) mod (hi - lo + 1)   (exactly representable in bf16)
+Every value is rounded binary64 -> binary32 (nearest even) -> bf16 (nearest even).
+Columns beyond ``cols`` in a padded row (pitch ``ld`` > cols) hold a quiet-NaN pattern, so
+a kernel that reads past K poisons its output.
+"""
+from __future__ import annotations
+
+import hashlib
+
+import numpy as np
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+PAD_BITS = 0x7FC0          # bf16 quiet NaN written into row padding
+_CHUNK = 1 << 22           # elements per generation chunk (bounds temporaries)
+
+
+def _mix64(z: np.ndarray, tmp: np.ndarray | None = None) -> np.ndarray:
+    """SplitMix64's output function, in place on z (uint64); returns z."""
+    if tmp is None:
+        tmp = np.empty_like(z)
+    with np.errstate(over="ignore"):
+        np.right_shift(z, np.uint64(30), out=tmp)
+        np.bitwise_xor(z, tmp, out=z)
+        np.multiply(z, _M1, out=z)
+        np.right_shift(z, np.uint64(27), out=tmp)
+        np.bitwise_xor(z, tmp, out=z)
+        np.multiply(z, _M2, out=z)
+        np.right_shift(z, np.uint64(31), out=tmp)
+        np.bitwise_xor(z, tmp, out=z)
+    return z
+
+
+def _key(seed: int) -> np.uint64:
+    return _mix64(np.array([seed & 0xFFFFFFFFFFFFFFFF], dtype=np.uint64))[0]
+
+
+def draws(seed: int, start: int, count: int, out: np.ndarray | None = None,
+          tmp: np.ndarray | None = None) -> np.ndarray:
+    """Raw 64-bit draws with counters start .. start+count-1 (optionally into ``out``)."""
+    z = np.empty(count, dtype=np.uint64) if out is None else out[:count]
+    t = None if tmp is None else tmp[:count]
+    z[:] = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        np.multiply(z, GAMMA, out=z)
+        np.add(z, _key(seed), out=z)
+    return _mix64(z, t)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """binary32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+class _Work:
+    """Scratch buffers reused across chunks (fresh allocations are the slow part)."""
+
+    def __init__(self, n: int):
+        self.z = np.empty(2 * n, dtype=np.uint64)
+        self.t = np.empty(2 * n, dtype=np.uint64)
+        self.f = np.empty(n, dtype=np.float64)
+        self.g = np.empty(n, dtype=np.float64)
+        self.h = np.empty(n, dtype=np.float64)
+
+
+def _values(kind: str, seed: int, start: int, count: int, p, w: _Work | None = None):
+    """binary64 values of elements start .. start+count-1 (a view into ``w``)."""
+    w = _Work(count) if w is None else w
+    f, g, h = w.f[:count], w.g[:count], w.h[:count]
+    if kind == "uniform":
+        lo, hi = p
+        z = draws(seed, start, count, w.z, w.t)
+        np.right_shift(z, np.uint64(40), out=z)
+        f[:] = z
+        np.multiply(f, (hi - lo) * 2.0 ** -24, out=f)
+        np.add(f, lo, out=f)
+        return f
+    if kind == "normal":
+        (sigma,) = p
+        z = draws(seed, 2 * start, 2 * count, w.z, w.t)
+        np.right_shift(z, np.uint64(11), out=z)
+        f[:] = z[0::2]                     # u1 = (z1 + 1) 2^-53 in (0, 1]
+        np.add(f, 1.0, out=f)
+        np.multiply(f, 2.0 ** -53, out=f)
+        g[:] = z[1::2]                     # u2 = z2 2^-53 in [0, 1)
+        np.multiply(g, 2.0 ** -53, out=g)
+        np.log(f, out=f)                   # r = sigma sqrt(-2 ln u1)
+        np.multiply(f, -2.0, out=f)
+        np.sqrt(f, out=f)
+        np.multiply(f, sigma, out=f)
+        np.multiply(g, 2.0 * np.pi, out=h)  # cos(2 pi u2)
+        np.cos(h, out=h)
+        np.multiply(f, h, out=f)
+        return f
+    if kind == "integer":
+        lo, hi = p
+        z = draws(seed, start, count, w.z, w.t)
+        np.right_shift(z, np.uint64(32), out=z)
+        np.remainder(z, np.uint64(hi - lo + 1), out=z)
+        f[:] = z
+        np.add(f, lo, out=f)
+        return f
+    raise ValueError(f"unknown distribution {kind!r}")
+
+
+def operand(kind: str, rows: int, cols: int, seed: int, params=(), ld: int | None = None,
+            row_offset: int = 0) -> np.ndarray:
+    """A rows x ld uint16 array of bf16 bit patterns; columns >= cols are NaN padding.
+
+    ``row_offset`` regenerates rows row_offset .. row_offset+rows-1 of a larger operand.
+    """
+    ld = cols if ld is None else ld
+    if ld < cols:
+        raise ValueError("ld < cols")
+    out = np.full((rows, ld), PAD_BITS, dtype=np.uint16)
+    if rows == 0 or cols == 0:
+        return out
+    rows_per_chunk = max(1, _CHUNK // cols)
+    w = _Work(min(rows, rows_per_chunk) * cols)
+    f32 = np.empty(min(rows, rows_per_chunk) * cols, dtype=np.float32)
+    for r0 in range(0, rows, rows_per_chunk):
+        r1 = min(rows, r0 + rows_per_chunk)
+        n = (r1 - r0) * cols
+        v = _values(kind, seed, (row_offset + r0) * cols, n, params, w)
+        f32[:n] = v
+        out[r0:r1, :cols] = f32_to_bf16_bits(f32[:n]).reshape(r1 - r0, cols)
+    return out
+
+
+def uniform(rows, cols, seed, lo=-1.0, hi=1.0, ld=None):
+    return operand("uniform", rows, cols, seed, (lo, hi), ld)
+
+
+def normal(rows, cols, seed, sigma=1.0, ld=None):
+    return operand("normal", rows, cols, seed, (sigma,), ld)
+
+
+def integers(rows, cols, seed, lo=-4, hi=4, ld=None):
+    return operand("integer", rows, cols, seed, (lo, hi), ld)
+
+
+def sha256(x: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(x).tobytes()).hexdigest()
+
+
+# ---------------------------------------------------------------------------------------
+# The workloads.  Shapes, value distributions and output types of the five configurations
+# the GEMM is measured and checked on; seeds are 1000*cfg for A and 1000*cfg+1 for B, and
+# batch item b adds 2*b to both.
+# ---------------------------------------------------------------------------------------
+OUT_FP32, OUT_BF16 = 0, 1
+
+WORKLOADS = {
+    "single_tile_128": dict(cfg=1, M=128, N=128, K=128, batch=1,
+                            a=("uniform", (-1.0, 1.0)), b=("uniform", (-1.0, 1.0)),
+                            out=OUT_FP32),
+    "square_4096": dict(cfg=2, M=4096, N=4096, K=4096, batch=1,
+                        a=("normal", (1.0,)), b=("normal", (1.0,)), out=OUT_FP32),
+    "gemv_m1": dict(cfg=3, M=1, N=4096, K=4096, batch=1,
+                    a=("normal", (1.0,)), b=("normal", (0.02,)), out=OUT_FP32),
+    "gemv_m16": dict(cfg=3, M=16, N=4096, K=4096, batch=1,
+                     a=("normal", (1.0,)), b=("normal", (0.02,)), out=OUT_FP32),
+    "ffn_up_8192x14336x4096": dict(cfg=4, M=8192, N=14336, K=4096, batch=1,
+                                   a=("normal", (1.0,)), b=("normal", (0.02,)),
+                                   out=OUT_BF16),
+    "ffn_down_8192x4096x14336": dict(cfg=4, M=8192, N=4096, K=14336, batch=1,
+                                     a=("normal", (1.0,)), b=("normal", (0.02,)),
+                                     out=OUT_BF16),
+    "irregular_3000x5000x4100": dict(cfg=5, M=3000, N=5000, K=4100, batch=1,
+                                     a=("uniform", (-1.0, 1.0)), b=("uniform", (-1.0, 1.0)),
+                                     out=OUT_FP32),
+    "batched_64x256x256x1024": dict(cfg=5, M=256, N=256, K=1024, batch=64,
+                                    a=("uniform", (-1.0, 1.0)), b=("uniform", (-1.0, 1.0)),
+                                    out=OUT_FP32),
+}
+
+
+def seeds(cfg: int, item: int = 0):
+    return 1000 * cfg + 2 * item, 1000 * cfg + 1 + 2 * item
+
+
+def make_operands(name: str, item: int = 0, lda=None, ldb=None, rows=None, row_offset=0):
+    """(A, B) bit-pattern arrays of workload ``name`` (batch item ``item``).
+
+    ``rows``/``row_offset`` restrict A to a band of rows (for sampled checks at full size).
+    """
+    w = WORKLOADS[name]
+    sa, sb = seeds(w["cfg"], item)
+    M = w["M"] if rows is None else rows
+    A = operand(w["a"][0], M, w["K"], sa, w["a"][1], lda, row_offset=row_offset)
+    B = operand(w["b"][0], w["N"], w["K"], sb, w["b"][1], ldb)
+    return A, B
