@@ -1,0 +1,148 @@
+/*
+ * gemm_bf16.h -- C ABI of libgemm_bf16.so, a tiled bf16 GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the matrix product that the page "读书笔记-《面向机器学习系统的现代 GPU
+ * 编程》" builds in its section "9 步优化" (steps 1-3 define it: output tiles, a loop over K
+ * blocks accumulating into one fp32 accumulator, a 2-D grid of tiles; steps 4-9 only make it
+ * faster), with both operands in the k-major layout named in that page's section
+ * "三个核心概念：scope、layout、dispatch":
+ *
+ *     C[i*ldc + j] = sum_{k<K} A[i*lda + k] * B[j*ldb + k]      0 <= i < M, 0 <= j < N
+ *
+ * i.e. C = A * B^T with A (M x K) and B (N x K) row-major bf16, each product exact and the
+ * sum accumulated in fp32; C (M x N, row-major) is OVERWRITTEN (no alpha/beta).  The order
+ * of the fp32 additions is not specified, but it is fixed: no kernel splits K across
+ * workgroups or uses atomics, so repeated calls with the same arguments give bitwise
+ * identical results.
+ *
+ * Memory and ownership.  A, B and C are device pointers (e.g. from hipMalloc or a torch
+ * tensor's data_ptr() on ROCm) owned by the caller; the library keeps no pointer after a call
+ * returns and allocates no memory in any call.  bf16 values are raw 16-bit patterns
+ * (uint16_t).  Pitches (lda, ldb, ldc) and batch strides are in ELEMENTS.  A and B must be
+ * 2-byte aligned, C 4-byte (fp32 out) or 2-byte (bf16 out) aligned; 16-byte aligned operands
+ * with pitches and K multiples of 8 take the fast kernels, anything else a slower general
+ * kernel with the same result semantics.  C must not overlap A or B.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void*; NULL is the default stream.  Calls are
+ * asynchronous: they enqueue kernels and return.  A device fault surfaces at the caller's
+ * next synchronisation, not in the return value.
+ *
+ * Errors.  Every function returns GEMM_OK (0) or a GEMM_ERR_* code; argument errors are
+ * detected on the host before anything is enqueued, and nothing is written then.  No C++
+ * exception crosses this interface.  gemm_bf16_status_string() names a code.
+ */
+#ifndef GEMM_BF16_H
+#define GEMM_BF16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define GEMM_OK 0
+#define GEMM_ERR_ARG 1         /* negative size, pitch < required, bad stride or variant  */
+#define GEMM_ERR_NULL 2        /* NULL pointer for an operand with a nonzero extent        */
+#define GEMM_ERR_DTYPE 3       /* out_dtype is not GEMM_OUT_FP32 or GEMM_OUT_BF16          */
+#define GEMM_ERR_ARCH 4        /* current device is not gfx950, or no device               */
+#define GEMM_ERR_LAUNCH 5      /* the HIP runtime rejected the kernel launch              */
+#define GEMM_ERR_UNSUPPORTED 6 /* the requested variant cannot run these arguments         */
+
+/* Output element types. */
+#define GEMM_OUT_FP32 0        /* C is float                                              */
+#define GEMM_OUT_BF16 1        /* C is bf16, rounded to nearest even from the fp32 sum   */
+
+/* Kernel variants (gemm_bf16_variant): the rungs of the page's nine-step ladder as built
+ * for gfx950.  GEMM_VARIANT_AUTO is what gemm_bf16 uses. */
+#define GEMM_VARIANT_AUTO 0
+#define GEMM_VARIANT_SIMPLE 1      /* steps 1-3: LDS-tiled 64x64, K loop, 2-D grid, fp32 VALU */
+#define GEMM_VARIANT_MFMA 2        /* MFMA register-blocked accumulators, one LDS stage       */
+#define GEMM_VARIANT_PIPELINED 3   /* steps 4-5: direct-to-LDS swizzled multi-stage ring       */
+#define GEMM_VARIANT_PERSISTENT 4  /* step 6: + persistent workgroups, XCD-aware tile order    */
+#define GEMM_VARIANT_SPECIALIZED 5 /* steps 7-9: producer/consumer waves sharing the B tile    */
+#define GEMM_VARIANT_GEMV 6        /* skinny M (M <= 16): bandwidth-bound decode path         */
+
+/*
+ * C = A * B^T for one problem (definition above).
+ *   M, N, K      >= 0.  M == 0 or N == 0: nothing is done.  K == 0: C is set to zero (the
+ *                empty sum).
+ *   A, lda       M x K bf16, row pitch lda >= max(K, 1).
+ *   B, ldb       N x K bf16, row pitch ldb >= max(K, 1).
+ *   C, ldc       M x N output, row pitch ldc >= max(N, 1); element type from out_dtype.
+ *   out_dtype    GEMM_OUT_FP32 or GEMM_OUT_BF16.
+ *   stream       hipStream_t or NULL.
+ * Returns GEMM_OK or GEMM_ERR_{ARG,NULL,DTYPE,ARCH,LAUNCH}.
+ */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const void* A, int64_t lda,
+              const void* B, int64_t ldb,
+              void* C, int64_t ldc,
+              int out_dtype, void* stream);
+
+/*
+ * `batch` independent problems of one shape: item b uses A + b*strideA, B + b*strideB and
+ * C + b*strideC (strides in elements, >= 0; A or B may be shared with stride 0).  Output
+ * items must not overlap: strideC >= (M-1)*ldc + N when batch > 1.  The whole batch is one
+ * launch whose tile scheduler enumerates (item, tile row, tile column).
+ * batch <= 65535.  Other arguments and errors as gemm_bf16.
+ */
+int gemm_bf16_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                              const void* A, int64_t lda, int64_t strideA,
+                              const void* B, int64_t ldb, int64_t strideB,
+                              void* C, int64_t ldc, int64_t strideC,
+                              int out_dtype, void* stream);
+
+/*
+ * As gemm_bf16_strided_batched, forcing one GEMM_VARIANT_* kernel (for ablations and the
+ * measurements of each rung).  A variant whose preconditions the arguments do not meet
+ * (GEMV with M > 16; the pipelined and persistent variants need 16-byte aligned A and B,
+ * lda, ldb, strides and K multiples of 8) returns GEMM_ERR_UNSUPPORTED and does nothing.
+ * An unknown variant returns GEMM_ERR_ARG.
+ */
+int gemm_bf16_variant(int variant, int64_t batch, int64_t M, int64_t N, int64_t K,
+                      const void* A, int64_t lda, int64_t strideA,
+                      const void* B, int64_t ldb, int64_t strideB,
+                      void* C, int64_t ldc, int64_t strideC,
+                      int out_dtype, void* stream);
+
+/*
+ * Host-only argument check of gemm_bf16_strided_batched (pass batch = 1 and zero strides
+ * for a single problem).  Touches no device and no pointer target: usable without a GPU.
+ * Returns GEMM_OK or GEMM_ERR_{ARG,NULL,DTYPE}.
+ */
+int gemm_bf16_validate(int64_t batch, int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t lda, int64_t strideA,
+                       const void* B, int64_t ldb, int64_t strideB,
+                       const void* C, int64_t ldc, int64_t strideC,
+                       int out_dtype);
+
+/*
+ * Host-only: the kernel gemm_bf16_variant(variant, ...) would launch for these arguments
+ * on a device with `num_cus` compute units (pass 0 for the MI355X's 256), and its launch
+ * shape.  Pointers are used only for their alignment.  On success *kernel_id receives a
+ * kernel id (see gemm_bf16_kernel_name), *grid_x the number of workgroups and *block the
+ * threads per workgroup; any output pointer may be NULL.  Returns the status the call would
+ * return before launching.
+ */
+int gemm_bf16_plan(int variant, int64_t batch, int64_t M, int64_t N, int64_t K,
+                   const void* A, int64_t lda, int64_t strideA,
+                   const void* B, int64_t ldb, int64_t strideB,
+                   const void* C, int64_t ldc, int64_t strideC,
+                   int out_dtype, int num_cus,
+                   int* kernel_id, int64_t* grid_x, int* block);
+
+/* Name of a kernel id from gemm_bf16_plan ("?" if unknown).  Static storage. */
+const char* gemm_bf16_kernel_name(int kernel_id);
+
+/* Human-readable name of a status code.  Static storage. */
+const char* gemm_bf16_status_string(int status);
+
+/* Library interface version (incremented on any change to this header). */
+int gemm_bf16_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_BF16_H */

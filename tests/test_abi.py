@@ -1,0 +1,111 @@
+"""The C-ABI library on the host: it loads, exports every function include/gemm_bf16.h
+declares, validates arguments with the documented codes, and plans the documented kernels.
+No GPU (validation and planning are host-only functions)."""
+import ctypes
+
+import pytest
+
+import tiled_matmul_amd as tm
+
+P = 1 << 12   # a fake, 16-byte aligned "device" address: validation never dereferences it
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tm.library()
+    names = tm.declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_version_and_strings():
+    assert tm.gemm_bf16_version() == 1
+    for s in range(7):
+        assert tm.gemm_bf16_status_string(s).startswith("GEMM_")
+    assert tm.gemm_bf16_status_string(99) == "unknown status"
+    assert tm.gemm_bf16_kernel_name(4) == "pipe_256"
+
+
+def v(batch=1, M=64, N=64, K=64, A=P, lda=None, sA=0, B=P, ldb=None, sB=0, C=P, ldc=None, sC=0,
+      out=0):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return tm.gemm_bf16_validate(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, out)
+
+
+def test_validate_ok_cases():
+    assert v() == tm.GEMM_OK
+    assert v(K=0, lda=1, ldb=1) == tm.GEMM_OK
+    assert v(M=0, C=None, A=None) == tm.GEMM_OK          # nothing to do: pointers unused
+    assert v(batch=0, C=None) == tm.GEMM_OK
+    assert v(K=0, lda=1, ldb=1, A=None, B=None) == tm.GEMM_OK   # empty sum needs only C
+    assert v(batch=3, sA=0, sB=64 * 64, sC=64 * 64) == tm.GEMM_OK
+    assert v(out=1, C=P + 2) == tm.GEMM_OK               # bf16 out needs 2-byte alignment
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), tm.GEMM_ERR_ARG), (dict(N=-1), tm.GEMM_ERR_ARG), (dict(K=-1), tm.GEMM_ERR_ARG),
+    (dict(lda=63), tm.GEMM_ERR_ARG), (dict(ldb=63), tm.GEMM_ERR_ARG),
+    (dict(ldc=63), tm.GEMM_ERR_ARG), (dict(K=0, lda=0), tm.GEMM_ERR_ARG),
+    (dict(batch=-1), tm.GEMM_ERR_ARG), (dict(batch=65536), tm.GEMM_ERR_ARG),
+    (dict(batch=2, sC=64 * 64 - 1), tm.GEMM_ERR_ARG), (dict(sA=-8), tm.GEMM_ERR_ARG),
+    (dict(A=None), tm.GEMM_ERR_NULL), (dict(B=None), tm.GEMM_ERR_NULL),
+    (dict(C=None), tm.GEMM_ERR_NULL), (dict(out=2), tm.GEMM_ERR_DTYPE),
+    (dict(out=-1), tm.GEMM_ERR_DTYPE), (dict(A=P + 1), tm.GEMM_ERR_ARG),
+    (dict(C=P + 2), tm.GEMM_ERR_ARG), (dict(M=1 << 41), tm.GEMM_ERR_ARG),
+])
+def test_validate_error_codes(kw, code):
+    assert v(**kw) == code
+
+
+def plan(variant=0, batch=1, M=4096, N=4096, K=4096, A=P, lda=None, sA=0, B=P, ldb=None, sB=0,
+         C=P, ldc=None, sC=0, out=0, cus=256):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return tm.gemm_bf16_plan(variant, batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, out, cus)
+
+
+def test_plan_workloads():
+    assert plan()[:2] == (0, "persist_256")
+    assert plan(M=1)[:2] == (0, "gemv")
+    assert plan(M=16)[:2] == (0, "gemv")
+    assert plan(M=17)[1] != "gemv"
+    assert plan(M=8192, N=14336, K=4096, out=1)[:2] == (0, "persist_256")
+    # K = 4100 with lda = 4100: rows are only 8-byte aligned -> general MFMA kernel
+    assert plan(M=3000, N=5000, K=4100)[1] == "mfma_128"
+    assert plan(batch=64, M=256, N=256, K=1024, sA=256 * 1024, sB=256 * 1024,
+                sC=256 * 256)[1] == "persist_128"
+    assert plan(K=0, lda=1, ldb=1)[:2] == (0, "zero_fill")
+    assert plan(M=0)[1] == "none"
+
+
+def test_plan_persistent_grid_is_cu_count():
+    rc, name, grid, block = plan(variant=4, M=8192, N=14336, K=4096)
+    assert (rc, name, grid, block) == (0, "persist_256", 256, 256)
+    rc, name, grid, _ = plan(variant=3, M=8192, N=14336, K=4096)
+    assert (rc, name, grid) == (0, "pipe_256", 32 * 56)
+
+
+def test_plan_variant_preconditions():
+    assert plan(variant=6, M=17)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=3, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=4, A=P + 2)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=7)[0] == tm.GEMM_ERR_ARG
+    assert plan(variant=1)[1] == "simple_64"
+    assert plan(variant=2)[1] == "mfma_128"
+
+
+def test_calls_fail_cleanly_without_gfx950():
+    """On a host without a gfx950 the launch path reports GEMM_ERR_ARCH, after validation."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    lib = tm.library()
+    assert lib.gemm_bf16(64, 64, 64, P, 64, P, 64, P, 64, 0, None) == tm.GEMM_ERR_ARCH
+    assert lib.gemm_bf16(64, 64, 64, P, 63, P, 64, P, 64, 0, None) == tm.GEMM_ERR_ARG

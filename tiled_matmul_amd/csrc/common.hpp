@@ -1,0 +1,153 @@
+// Shared device-side building blocks of the gfx950 GEMM kernels: vector types, the bf16
+// conversions, the buffer-resource helpers used by the direct-to-LDS loads, and the
+// XCD-aware tile order.  Internal to libgemm_bf16.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tmm {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+enum { OUT_F32 = 0, OUT_BF16 = 1 };
+
+// Problem description handed to every kernel by value.  Pointers are device pointers;
+// leading dimensions and batch strides are in elements.
+struct GemmArgs {
+    int64_t batch, M, N, K;
+    const uint16_t* A;
+    int64_t lda, sA;
+    const uint16_t* B;
+    int64_t ldb, sB;
+    void* C;
+    int64_t ldc, sC;
+};
+
+// Tile grid of one launch: tiles_m x tiles_n tiles per batch item, `total` over the batch.
+struct TileGrid {
+    int tiles_m, tiles_n, total, group_m;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    __bf16 b = static_cast<__bf16>(x);
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Buffer resource over [base, base + bytes): raw (stride 0) addressing, so a lane whose
+// offset is >= bytes reads zeros.  The fourth dword is the gfx9 raw-buffer format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// An offset no buffer of this library reaches (buffers are capped below 2^31 bytes).
+constexpr uint32_t OOB = 0x80000000u;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from global (through the buffer resource) straight into LDS at
+// lds_base + 16 * lane; lds_base must be wave-uniform.
+__device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                            uint32_t voffset, uint32_t soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, voffset, soffset, 0, 0);
+}
+
+// Map a linear work index to a tile so that the workgroups one XCD runs get neighbouring
+// tiles.  Workgroup ids are handed to the 8 XCDs round-robin, so index t runs on XCD t % 8;
+// the bijection below gives XCD x a contiguous range of logical tiles, which are then
+// rastered in groups of `group_m` tile rows so that the A and B panels they share stay in
+// that XCD's L2.
+__device__ __forceinline__ void tile_of(int t, const TileGrid& g, int& batch, int& tm, int& tn) {
+    constexpr int XCD = 8;
+    int per = g.total / XCD, extra = g.total % XCD;
+    int x = t % XCD, local = t / XCD;
+    int L = (x < extra) ? x * (per + 1) + local : extra * (per + 1) + (x - extra) * per + local;
+    int tiles = g.tiles_m * g.tiles_n;
+    batch = L / tiles;
+    int r = L - batch * tiles;
+    int group = g.group_m * g.tiles_n;
+    int first_m = (r / group) * g.group_m;
+    int gm = min(g.tiles_m - first_m, g.group_m);
+    int within = r % group;
+    tm = first_m + within % gm;
+    tn = within / gm;
+}
+
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Workgroup barrier with no memory fence: the callers wait for their own loads with an
+// explicit s_waitcnt first.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+}  // namespace tmm
+
+namespace tmm {
+
+// Write a wave's register-blocked accumulator to C.  The MFMA was issued with the B tile as
+// its first operand and the A tile as its second, so accumulator fragment [fi][fj] holds
+// D[n][m] = C[m][n] for a 16 (n) x 16 (m) block, and lane l, register r carries
+//     m = m_base + 16*fj + (l % 16),   n = n_base + 16*fi + 4*(l / 16) + r,
+// i.e. four consecutive n of one C row: one 16-byte (fp32) or 8-byte (bf16) store.
+// `vec_ok`: C's base and pitch allow those vector stores.  Elements outside M x N are
+// skipped.
+template <int OUT, int FN, int FM>
+__device__ __forceinline__ void store_acc(void* Cp, int64_t ldc, int64_t M, int64_t N,
+                                          int64_t m_base, int64_t n_base,
+                                          const f32x4 (&acc)[FN][FM], bool vec_ok) {
+    const int lane = lane_id();
+    const bool full = vec_ok && (m_base + 16 * FM <= M) && (n_base + 16 * FN <= N);
+#pragma unroll
+    for (int fj = 0; fj < FM; ++fj) {
+        const int64_t m = m_base + 16 * fj + (lane & 15);
+#pragma unroll
+        for (int fi = 0; fi < FN; ++fi) {
+            const int64_t n = n_base + 16 * fi + 4 * (lane >> 4);
+            const f32x4 v = acc[fi][fj];
+            if (full) {
+                if constexpr (OUT == OUT_F32) {
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(Cp) + m * ldc + n) = v;
+                } else {
+                    u32x2 p = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cp) + m * ldc + n) = p;
+                }
+            } else if (m < M) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (n + r < N) {
+                        if constexpr (OUT == OUT_F32)
+                            static_cast<float*>(Cp)[m * ldc + n + r] = v[r];
+                        else
+                            static_cast<uint16_t*>(Cp)[m * ldc + n + r] = f32_to_bf16(v[r]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace tmm

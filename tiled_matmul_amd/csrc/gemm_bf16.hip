@@ -1,0 +1,302 @@
+// The C ABI of libgemm_bf16.so (declared in include/gemm_bf16.h): argument validation, the
+// planner that picks a kernel and launch shape, the gfx950 device check, and the launches.
+// No device memory is allocated here or anywhere in the library.
+#include <mutex>
+#include <string.h>
+
+#include "gemm_bf16.h"
+#include "launch.hpp"
+
+using namespace tmm;
+
+namespace {
+
+constexpr int kVersion = 1;
+constexpr int kDefaultCUs = 256;        // MI355X
+constexpr int64_t kMaxBatch = 65535;
+constexpr int64_t k2G = int64_t(1) << 31;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// --- device check ------------------------------------------------------------------------
+struct DevInfo {
+    bool known = false;
+    bool ok = false;
+    int cus = 0;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+// GEMM_OK and the CU count of the current device if it is a gfx950, else GEMM_ERR_ARCH.
+int current_device(int* cus) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_ERR_ARCH;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DevInfo& d = g_dev[dev];
+    if (!d.known) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_ARCH;
+        d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.cus = prop.multiProcessorCount;
+        d.known = true;
+    }
+    if (!d.ok) return GEMM_ERR_ARCH;
+    *cus = d.cus;
+    return GEMM_OK;
+}
+
+// --- validation --------------------------------------------------------------------------
+int validate(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+             int64_t sA, const void* B, int64_t ldb, int64_t sB, const void* C, int64_t ldc,
+             int64_t sC, int out) {
+    if (out != GEMM_OUT_FP32 && out != GEMM_OUT_BF16) return GEMM_ERR_DTYPE;
+    if (batch < 0 || batch > kMaxBatch || M < 0 || N < 0 || K < 0) return GEMM_ERR_ARG;
+    const int64_t big = int64_t(1) << 40;   // keeps every index product inside int64
+    if (M > big || N > big || K > big || lda > big || ldb > big || ldc > big) return GEMM_ERR_ARG;
+    if (sA > big || sB > big || sC > big) return GEMM_ERR_ARG;
+    if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1)) return GEMM_ERR_ARG;
+    if (sA < 0 || sB < 0 || sC < 0) return GEMM_ERR_ARG;
+    if (batch == 0 || M == 0 || N == 0) return GEMM_OK;
+    if (batch > 1 && sC < (M - 1) * ldc + N) return GEMM_ERR_ARG;
+    // every tile id must fit in a 32-bit int (the smallest tile is 64 x 64)
+    if (cdiv(M, 64) >= k2G || cdiv(N, 64) >= k2G) return GEMM_ERR_ARG;
+    if (static_cast<__int128>(cdiv(M, 64)) * cdiv(N, 64) * batch >= k2G) return GEMM_ERR_ARG;
+    if (C == nullptr) return GEMM_ERR_NULL;
+    if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL;
+    if (!aligned(A, 2) || !aligned(B, 2)) return GEMM_ERR_ARG;
+    if (!aligned(C, out == GEMM_OUT_FP32 ? 4 : 2)) return GEMM_ERR_ARG;
+    return GEMM_OK;
+}
+
+// --- planner -----------------------------------------------------------------------------
+struct Shape {
+    int64_t batch, M, N, K, lda, sA, ldb, sB, ldc, sC;
+    const void *A, *B, *C;
+    int out;
+};
+
+// The direct-to-LDS kernels: 16-byte chunks that never straddle K, 32-bit buffer offsets.
+bool fast_loads_ok(const Shape& s, int rows) {
+    if (!aligned(s.A, 16) || !aligned(s.B, 16)) return false;
+    if (s.lda % 8 || s.ldb % 8 || s.K % 8) return false;
+    if (s.batch > 1 && (s.sA % 8 || s.sB % 8)) return false;
+    return int64_t(rows) * s.lda * 2 < k2G && int64_t(rows) * s.ldb * 2 < k2G;
+}
+
+bool vec_store_ok(const Shape& s) {
+    const uintptr_t a = s.out == GEMM_OUT_FP32 ? 16 : 8;
+    return aligned(s.C, a) && s.ldc % 4 == 0 && (s.batch == 1 || s.sC % 4 == 0);
+}
+
+int widest_vec(const Shape& s) {
+    for (int v = 8; v > 1; v /= 2) {
+        if (aligned(s.A, 2 * v) && aligned(s.B, 2 * v) && s.lda % v == 0 && s.ldb % v == 0 &&
+            s.K % v == 0 && (s.batch == 1 || (s.sA % v == 0 && s.sB % v == 0)))
+            return v;
+    }
+    return 1;
+}
+
+void tile_grid(const Shape& s, int bm, int bn, Plan& p) {
+    p.grid.tiles_m = static_cast<int>(cdiv(s.M, bm));
+    p.grid.tiles_n = static_cast<int>(cdiv(s.N, bn));
+    p.grid.total = static_cast<int>(p.grid.tiles_m * int64_t(p.grid.tiles_n) * s.batch);
+    p.grid.group_m = 4;
+}
+
+// 2-D grid launches (tile column, tile row, batch item) of the generic kernels.
+int plan_2d(const Shape& s, int kernel, int tile, Plan& p) {
+    const int64_t tm = cdiv(s.M, tile), tn = cdiv(s.N, tile);
+    if (tm > 65535 || tn >= k2G) return GEMM_ERR_UNSUPPORTED;
+    p.kernel = kernel;
+    p.grid_x = static_cast<int>(tn);
+    p.grid_y = static_cast<int>(tm);
+    p.grid_z = static_cast<int>(s.batch);
+    p.block = 256;
+    p.vec = widest_vec(s);
+    p.vec_store = vec_store_ok(s);
+    return GEMM_OK;
+}
+
+// Tile size of the pipelined kernels: 256 x 256 when that still gives most CUs a tile,
+// otherwise 128 x 128.
+bool use_big_tile(const Shape& s, int cus) {
+    const int64_t big = cdiv(s.M, 256) * cdiv(s.N, 256) * s.batch;
+    return big * 10 >= int64_t(cus) * 9;
+}
+
+int plan_pipe(const Shape& s, bool persistent, int cus, Plan& p) {
+    const bool big = use_big_tile(s, cus);
+    if (!fast_loads_ok(s, big ? 256 : 128)) return GEMM_ERR_UNSUPPORTED;
+    tile_grid(s, big ? 256 : 128, big ? 256 : 128, p);
+    p.kernel = persistent ? (big ? K_PERSIST_256 : K_PERSIST_128) : (big ? K_PIPE_256 : K_PIPE_128);
+    p.grid_x = persistent ? std::min(p.grid.total, cus) : p.grid.total;
+    p.grid_y = p.grid_z = 1;
+    p.block = 256;
+    p.vec_store = vec_store_ok(s);
+    return GEMM_OK;
+}
+
+bool gemv_ok(const Shape& s) {
+    if (s.M > 16 || s.batch != 1) return false;
+    if (!aligned(s.A, 16) || !aligned(s.B, 16) || s.lda % 8 || s.ldb % 8 || s.K % 8) return false;
+    return 16 * s.lda * 2 < k2G && 16 * s.ldb * 2 < k2G && cdiv(s.N, 16) < k2G;
+}
+
+int plan_gemv(const Shape& s, Plan& p) {
+    if (!gemv_ok(s)) return GEMM_ERR_UNSUPPORTED;
+    p.kernel = K_GEMV;
+    p.grid_x = static_cast<int>(cdiv(s.N, 16));
+    p.grid_y = p.grid_z = 1;
+    p.block = 512;
+    return GEMM_OK;
+}
+
+int make_plan(int variant, const Shape& s, int cus, Plan& p) {
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_GEMV) return GEMM_ERR_ARG;
+    p = Plan{};
+    if (s.batch == 0 || s.M == 0 || s.N == 0) {
+        p.kernel = K_NONE;
+        return GEMM_OK;
+    }
+    if (s.K == 0) {  // every variant: the empty sum
+        p.kernel = K_ZERO_FILL;
+        p.grid_x = static_cast<int>(std::min<int64_t>(cdiv(s.M * s.N * s.batch, 256), 65536));
+        p.grid_y = p.grid_z = 1;
+        p.block = 256;
+        return GEMM_OK;
+    }
+    switch (variant) {
+        case GEMM_VARIANT_SIMPLE: return plan_2d(s, K_SIMPLE_64, 64, p);
+        case GEMM_VARIANT_MFMA: return plan_2d(s, K_MFMA_128, 128, p);
+        case GEMM_VARIANT_PIPELINED: return plan_pipe(s, false, cus, p);
+        case GEMM_VARIANT_PERSISTENT: return plan_pipe(s, true, cus, p);
+        case GEMM_VARIANT_SPECIALIZED: return GEMM_ERR_UNSUPPORTED;
+        case GEMM_VARIANT_GEMV: return plan_gemv(s, p);
+        default: break;
+    }
+    // AUTO
+    if (gemv_ok(s)) return plan_gemv(s, p);
+    if (plan_pipe(s, true, cus, p) == GEMM_OK) return GEMM_OK;
+    int rc = plan_2d(s, K_MFMA_128, 128, p);
+    if (rc == GEMM_OK) return rc;
+    return GEMM_ERR_ARG;  // no kernel can take this shape (tile grid beyond launch limits)
+}
+
+int run(int variant, const Shape& s, void* stream) {
+    int rc = validate(s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC, s.out);
+    if (rc != GEMM_OK) return rc;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_GEMV) return GEMM_ERR_ARG;
+    if (s.batch == 0 || s.M == 0 || s.N == 0) return GEMM_OK;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != GEMM_OK) return rc;
+    Plan p;
+    rc = make_plan(variant, s, cus, p);
+    if (rc != GEMM_OK) return rc;
+    GemmArgs g{s.batch, s.M, s.N, s.K,
+               static_cast<const uint16_t*>(s.A), s.lda, s.sA,
+               static_cast<const uint16_t*>(s.B), s.ldb, s.sB,
+               const_cast<void*>(s.C), s.ldc, s.sC};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    switch (p.kernel) {
+        case K_NONE: return GEMM_OK;
+        case K_ZERO_FILL: e = launch_zero_fill(g, s.out, p, st); break;
+        case K_SIMPLE_64: e = launch_simple(g, s.out, p, st); break;
+        case K_MFMA_128: e = launch_mfma(g, s.out, p, st); break;
+        case K_PIPE_256:
+        case K_PIPE_128:
+        case K_PERSIST_256:
+        case K_PERSIST_128: e = launch_pipe(g, s.out, p, st); break;
+        case K_GEMV: e = launch_gemv(g, s.out, p, st); break;
+        default: return GEMM_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+Shape shape(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t sA,
+            const void* B, int64_t ldb, int64_t sB, const void* C, int64_t ldc, int64_t sC, int out) {
+    return Shape{batch, M, N, K, lda, sA, ldb, sB, ldc, sC, A, B, C, out};
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+              int64_t ldb, void* C, int64_t ldc, int out_dtype, void* stream) {
+    return run(GEMM_VARIANT_AUTO, shape(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, out_dtype), stream);
+}
+
+int gemm_bf16_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A,
+                              int64_t lda, int64_t strideA, const void* B, int64_t ldb,
+                              int64_t strideB, void* C, int64_t ldc, int64_t strideC,
+                              int out_dtype, void* stream) {
+    return run(GEMM_VARIANT_AUTO,
+               shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype), stream);
+}
+
+int gemm_bf16_variant(int variant, int64_t batch, int64_t M, int64_t N, int64_t K, const void* A,
+                      int64_t lda, int64_t strideA, const void* B, int64_t ldb, int64_t strideB,
+                      void* C, int64_t ldc, int64_t strideC, int out_dtype, void* stream) {
+    return run(variant, shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype),
+               stream);
+}
+
+int gemm_bf16_validate(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       int64_t strideA, const void* B, int64_t ldb, int64_t strideB, const void* C,
+                       int64_t ldc, int64_t strideC, int out_dtype) {
+    return validate(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype);
+}
+
+int gemm_bf16_plan(int variant, int64_t batch, int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, int64_t strideA, const void* B, int64_t ldb, int64_t strideB,
+                   const void* C, int64_t ldc, int64_t strideC, int out_dtype, int num_cus,
+                   int* kernel_id, int64_t* grid_x, int* block) {
+    int rc = validate(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype);
+    if (rc != GEMM_OK) return rc;
+    Plan p;
+    rc = make_plan(variant, shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype),
+                   num_cus > 0 ? num_cus : kDefaultCUs, p);
+    if (rc != GEMM_OK) return rc;
+    if (kernel_id) *kernel_id = p.kernel;
+    if (grid_x) *grid_x = int64_t(p.grid_x) * (p.grid_y ? p.grid_y : 1) * (p.grid_z ? p.grid_z : 1);
+    if (block) *block = p.block;
+    return GEMM_OK;
+}
+
+const char* gemm_bf16_kernel_name(int k) {
+    switch (k) {
+        case K_NONE: return "none";
+        case K_ZERO_FILL: return "zero_fill";
+        case K_SIMPLE_64: return "simple_64";
+        case K_MFMA_128: return "mfma_128";
+        case K_PIPE_256: return "pipe_256";
+        case K_PIPE_128: return "pipe_128";
+        case K_PERSIST_256: return "persist_256";
+        case K_PERSIST_128: return "persist_128";
+        case K_SPEC_256: return "spec_256";
+        case K_GEMV: return "gemv";
+        default: return "?";
+    }
+}
+
+const char* gemm_bf16_status_string(int status) {
+    switch (status) {
+        case GEMM_OK: return "GEMM_OK";
+        case GEMM_ERR_ARG: return "GEMM_ERR_ARG: invalid size, pitch, stride or variant";
+        case GEMM_ERR_NULL: return "GEMM_ERR_NULL: null pointer for an operand with nonzero extent";
+        case GEMM_ERR_DTYPE: return "GEMM_ERR_DTYPE: out_dtype must be GEMM_OUT_FP32 or GEMM_OUT_BF16";
+        case GEMM_ERR_ARCH: return "GEMM_ERR_ARCH: current device is not a gfx950 (MI355X)";
+        case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: the HIP runtime rejected the launch";
+        case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: variant cannot run these arguments";
+        default: return "unknown status";
+    }
+}
+
+int gemm_bf16_version(void) { return kVersion; }
+
+}  // extern "C"

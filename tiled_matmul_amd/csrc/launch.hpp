@@ -1,0 +1,42 @@
+// Host-side launchers of the kernel families, one per source file.  Each validates nothing
+// (gemm_bf16.cpp does that) and returns the launch status.  Internal to libgemm_bf16.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace tmm {
+
+// Kernel identifiers, reported by gemm_bf16_plan() and named by gemm_bf16_kernel_name().
+enum KernelId {
+    K_NONE = 0,
+    K_ZERO_FILL = 1,        // K == 0: C = 0
+    K_SIMPLE_64 = 2,        // ladder step 1: LDS-tiled, K loop, 2-D grid, fp32 VALU FMA
+    K_MFMA_128 = 3,         // ladder step 3: MFMA register-blocked, one LDS stage, register loads
+    K_PIPE_256 = 4,         // ladder step 2: direct-to-LDS ring, swizzle, 2-D grid, 256x256 tile
+    K_PIPE_128 = 5,         //   same, 128x128 tile
+    K_PERSIST_256 = 6,      // ladder step 4: persistent, XCD-aware grouped order, 256x256
+    K_PERSIST_128 = 7,      //   same, 128x128
+    K_SPEC_256 = 8,         // ladder step 5: wave-specialised, two consumer groups share B
+    K_GEMV = 9,             // ladder step 6: skinny-M bandwidth path
+    K_COUNT = 10
+};
+
+// Launch shape chosen for a problem (filled by the planner, consumed by the launchers).
+struct Plan {
+    int kernel = K_NONE;
+    int vec = 1;            // global load width in elements for K_MFMA_128 (8, 4, 2 or 1)
+    int vec_store = 0;      // C allows 16-byte (fp32) / 8-byte (bf16) stores
+    TileGrid grid{};
+    int grid_x = 0, grid_y = 0, grid_z = 0, block = 0;
+};
+
+hipError_t launch_zero_fill(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_simple(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_mfma(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_spec(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+
+}  // namespace tmm
