@@ -1,0 +1,301 @@
+"""Benchmark of the bf16 GEMM C = A * B^T on one MI355X.
+
+One step = one gemm_bf16 call (the whole GEMM: every tile, the full K loop, the epilogue)
+on one set of synthetic inputs already resident in device memory.  The headline workload
+is the square 4096^3 GEMM (bf16 inputs N(0,1), fp32 output); the decode GEMV
+(M=1, N=K=4096, fp32 output) is measured in a second leg and reported in "gemv".
+
+Timing: W untimed warm-up steps, then K steps between two torch.cuda.synchronize() calls,
+timed with HIP events recorded on the stream the kernels are launched on (the library
+launches on torch's current stream).  Inputs rotate over several buffer sets whose total
+exceeds the 256 MB Infinity Cache, so no step finds its operands in a cache left warm by
+the previous one.  The GEMV leg captures its launches in a HIP graph (one kernel is a few
+microseconds, below the Python launch overhead) and times graph replays.
+
+cpu_baseline: the CPU oracle (plain fp64 triple loop, OpenMP over rows) timed on a bounded
+sample of the same workload: a band of rows of C, all N columns, the full K.  Its rows are
+also compared with the GPU output under the acceptance bound.
+
+Prints ONE JSON line.  `python bench.py --gpus N` with N > 1 exits: this build measures
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import tiled_matmul_amd as tm  # noqa: E402
+from tiled_matmul_amd import roofline as rl  # noqa: E402
+from tiled_matmul_amd import synth  # noqa: E402
+
+HBM_TB_S = rl.MI355X_BF16.hbm_tb_s
+MFMA_TFLOPS = rl.MI355X_BF16.peak_tflops
+MALL_BYTES = 256 * 2 ** 20
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    """Hash of every HIP source and header: identifies the kernels a profile was taken on."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "tiled_matmul_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def to_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def make_sets(name, torch, min_bytes):
+    """Enough copies of the workload's operands (and outputs) to exceed min_bytes."""
+    w = synth.WORKLOADS[name]
+    M, N, K, out = w["M"], w["N"], w["K"], w["out"]
+    A, B = synth.make_operands(name)
+    Ad, Bd = to_dev(A, torch), to_dev(B, torch)
+    out_t = torch.float32 if out == tm.GEMM_OUT_FP32 else torch.bfloat16
+    per = Ad.numel() * 2 + Bd.numel() * 2 + M * N * (4 if out == tm.GEMM_OUT_FP32 else 2)
+    n = max(1, -(-min_bytes // per))
+    sets = []
+    for i in range(n):
+        a = Ad if i == 0 else Ad.clone()
+        b = Bd if i == 0 else Bd.clone()
+        sets.append((a, b, torch.empty((M, N), dtype=out_t, device="cuda")))
+    return (A, B), sets
+
+
+def time_steps(launch, nsets, steps, warmup, torch):
+    for i in range(warmup):
+        launch(i % nsets)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        launch(i % nsets)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def gemm_leg(args, torch):
+    name = args.workload
+    w = synth.WORKLOADS[name]
+    M, N, K, out = w["M"], w["N"], w["K"], w["out"]
+    log(f"[bench] generating {name} operands")
+    (A, B), sets = make_sets(name, torch, args.rotate_mb * 2 ** 20)
+    variant = tm.VARIANTS[args.variant]
+    rc, kname, grid, block = tm.gemm_bf16_plan(variant, 1, M, N, K, sets[0][0], K, 0,
+                                               sets[0][1], K, 0, sets[0][2], N, 0, out,
+                                               torch.cuda.get_device_properties(0).multi_processor_count)
+    if rc != 0:
+        raise SystemExit(f"variant {args.variant} cannot run {name}: {tm.gemm_bf16_status_string(rc)}")
+
+    def launch(i):
+        a, b, c = sets[i]
+        tm.gemm_bf16_variant(variant, 1, M, N, K, a, K, 0, b, K, 0, c, N, 0, out)
+
+    log(f"[bench] timing {name}: kernel {kname}, {len(sets)} rotating buffer sets, "
+        f"{args.warmup} warm-up + {args.steps} timed steps")
+    ms, wall = time_steps(launch, len(sets), args.steps, args.warmup, torch)
+    flops = rl.flops(M, N, K)
+    tflops = flops / (ms * 1e-3) / 1e12
+    obytes = 4 if out == tm.GEMM_OUT_FP32 else 2
+    return {
+        "name": name, "M": M, "N": N, "K": K, "out": "fp32" if out == 0 else "bf16",
+        "kernel": kname, "grid": grid, "block": block, "ms": ms, "wall_s": wall,
+        "tflops": tflops, "flops": flops,
+        "bytes": rl.algorithmic_bytes(M, N, K, obytes), "A": A, "B": B, "sets": sets,
+    }
+
+
+def gemv_leg(args, torch):
+    name = "gemv_m1"
+    w = synth.WORKLOADS[name]
+    M, N, K, out = w["M"], w["N"], w["K"], w["out"]
+    log("[bench] generating gemv_m1 operands")
+    (A, B), sets = make_sets(name, torch, 2 * MALL_BYTES + 32 * 2 ** 20)
+    n = len(sets)
+
+    def launch(i):
+        a, b, c = sets[i]
+        tm.gemm_bf16(M, N, K, a, K, b, K, c, N, out)
+
+    for i in range(n):      # fills the per-device cache before capture
+        launch(i)
+    torch.cuda.synchronize()
+    reps = max(1, args.gemv_launches // n)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        for r in range(reps):
+            for i in range(n):
+                launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.gemv_replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    launches = reps * n * args.gemv_replays
+    us = start.elapsed_time(end) * 1e3 / launches
+    nbytes = rl.algorithmic_bytes(M, N, K, 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    _, kname, grid, block = tm.gemm_bf16_plan(0, 1, M, N, K, sets[0][0], K, 0, sets[0][1], K, 0,
+                                              sets[0][2], N, 0, out)
+    return {
+        "metric": "GB/s and % of HBM peak, decode GEMV M=1 N=K=4096 (bf16 in, fp32 out)",
+        "value": gbs, "unit": "GB/s", "us_per_launch": us, "launches": launches,
+        "kernel": kname, "grid": grid, "block": block, "rotating_weight_buffers": n,
+        "timing": "HIP events around replays of a captured HIP graph of back-to-back launches",
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_TB_S * 1e3, "unit": "GB/s",
+                     "frac": gbs / (HBM_TB_S * 1e3), "traffic": traffic_for(kname, name),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+
+
+def cpu_baseline_leg(res, args, torch):
+    """The oracle, as it stands, on a band of rows of the same GEMM."""
+    import oracle
+    from oracle import check as ck
+    A, B, K, N = res["A"], res["B"], res["K"], res["N"]
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, rows=list(range(threads)), nthreads=threads)   # one row per thread
+    t_probe = max(time.perf_counter() - t0, 1e-3)
+    rows = int(min(res["M"], max(threads, args.cpu_seconds / t_probe * threads)))
+    rows = max(threads, (rows // threads) * threads)
+    sel = list(range(rows))
+    log(f"[bench] cpu_baseline: oracle on {rows} rows x {N} x {K} with {threads} threads")
+    t0 = time.perf_counter()
+    C_ref, Mag = oracle.gemm(A, B, rows=sel, nthreads=threads)
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    out = res["sets"][(args.warmup + args.steps - 1) % len(res["sets"])][2]
+    got = out[:rows].cpu()
+    got = got.numpy() if got.dtype == torch.float32 else got.view(torch.int16).numpy().view(np.uint16)
+    od = 0 if res["out"] == "fp32" else 1
+    par = ck.check(got, C_ref, Mag, K, od)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "seconds": t, "cpu_model": cpu_model,
+        "sample": f"rows 0..{rows - 1} of C ({rows} x {N} outputs, full K={K}) of the same "
+                  f"{res['M']}x{N}x{K} GEMM; fp64 triple loop, OpenMP over rows",
+        "parity_rows_checked": rows, "parity_max_err_over_bound": par["max_err_over_bound"],
+        "parity_ok": par["ok"],
+    }
+
+
+def copy_leg(args, torch):
+    """A plain device copy of known size (the calibration kernel for the byte counters)."""
+    n = args.copy_mb * 2 ** 20
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"leg": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "launches": args.steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="square_4096", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--variant", default="auto", choices=sorted(tm.VARIANTS))
+    ap.add_argument("--rotate-mb", type=int, default=512,
+                    help="total size of the rotating input/output sets")
+    ap.add_argument("--gemv-launches", type=int, default=340)
+    ap.add_argument("--gemv-replays", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target length of the cpu_baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--leg", default="all", choices=["all", "gemm", "copy"])
+    ap.add_argument("--copy-mb", type=int, default=1024)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the GEMM shards by columns of B with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    tm.library()
+
+    if args.leg == "copy":
+        copy_leg(args, torch)
+        return
+
+    res = gemm_leg(args, torch)
+    result = {
+        "metric": "bf16 GEMM TFLOP/s + % MFMA peak at 4096^3; GB/s % HBM peak at M=1",
+        "value": res["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{res['name']}: C = A B^T, M={res['M']} N={res['N']} "
+                               f"K={res['K']}, bf16 in, fp32 accumulate, {res['out']} out",
+                   "variant": args.variant, "kernel": res["kernel"],
+                   "grid": res["grid"], "block": res["block"],
+                   "rotating_buffer_sets": len(res["sets"])},
+        "pct_mfma_peak": 100.0 * res["tflops"] / MFMA_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": res["tflops"], "peak": MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": res["tflops"] / MFMA_TFLOPS,
+                     "traffic": traffic_for(res["kernel"], res["name"]),
+                     "flops_per_launch": res["flops"],
+                     "algorithmic_bytes_per_launch": res["bytes"]},
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    if args.leg == "all" and not args.no_gemv:
+        result["gemv"] = gemv_leg(args, torch)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_leg(res, args, torch)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
