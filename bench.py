@@ -251,7 +251,7 @@ def main():
                     help="target length of the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
-    ap.add_argument("--leg", default="all", choices=["all", "gemm", "copy"])
+    ap.add_argument("--leg", default="all", choices=["all", "gemm", "gemv", "copy"])
     ap.add_argument("--copy-mb", type=int, default=1024)
     args = ap.parse_args()
 
@@ -269,6 +269,9 @@ def main():
 
     if args.leg == "copy":
         copy_leg(args, torch)
+        return
+    if args.leg == "gemv":
+        print(json.dumps({"gemv": gemv_leg(args, torch), "kernel_source_sha": kernel_source_sha()}))
         return
 
     res = gemm_leg(args, torch)

@@ -69,11 +69,13 @@ def plan(variant=0, batch=1, M=4096, N=4096, K=4096, A=P, lda=None, sA=0, B=P, l
 
 
 def test_plan_workloads():
-    assert plan()[:2] == (0, "persist_256")
+    assert plan()[:2] == (0, "spec_256")
     assert plan(M=1)[:2] == (0, "gemv")
     assert plan(M=16)[:2] == (0, "gemv")
     assert plan(M=17)[1] != "gemv"
-    assert plan(M=8192, N=14336, K=4096, out=1)[:2] == (0, "persist_256")
+    assert plan(M=8192, N=14336, K=4096, out=1)[:2] == (0, "spec_256")
+    assert plan(variant=5)[:2] == (0, "spec_256")
+    assert plan(variant=5)[3] == 512
     # K = 4100 with lda = 4100: rows are only 8-byte aligned -> general MFMA kernel
     assert plan(M=3000, N=5000, K=4100)[1] == "mfma_128"
     assert plan(batch=64, M=256, N=256, K=1024, sA=256 * 1024, sB=256 * 1024,
@@ -94,6 +96,7 @@ def test_plan_variant_preconditions():
     assert plan(variant=3, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
     assert plan(variant=4, A=P + 2)[0] == tm.GEMM_ERR_UNSUPPORTED
     assert plan(variant=7)[0] == tm.GEMM_ERR_ARG
+    assert plan(variant=5, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
     assert plan(variant=1)[1] == "simple_64"
     assert plan(variant=2)[1] == "mfma_128"
 

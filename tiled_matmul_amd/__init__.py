@@ -16,7 +16,9 @@ import os
 import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgemm_bf16.so")
+# GEMM_BF16_LIB selects another build of the same library (e.g. one compiled with other
+# tile-shape macros by tiled_matmul_amd.build.build_library(out=..., defines=...)).
+LIB_PATH = os.environ.get("GEMM_BF16_LIB") or os.path.join(_HERE, "libgemm_bf16.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gemm_bf16.h")
 
 GEMM_OK = 0

@@ -46,8 +46,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Buffer resource over [base, base + bytes): raw (stride 0) addressing, so a lane whose
@@ -121,28 +127,95 @@ __device__ __forceinline__ void store_acc(void* Cp, int64_t ldc, int64_t M, int6
                                           const f32x4 (&acc)[FN][FM], bool vec_ok) {
     const int lane = lane_id();
     const bool full = vec_ok && (m_base + 16 * FM <= M) && (n_base + 16 * FN <= N);
+    if constexpr (OUT == OUT_F32) {
+#pragma unroll
+        for (int fj = 0; fj < FM; ++fj) {
+            const int64_t m = m_base + 16 * fj + (lane & 15);
+#pragma unroll
+            for (int fi = 0; fi < FN; ++fi) {
+                const int64_t n = n_base + 16 * fi + 4 * (lane >> 4);
+                const f32x4 v = acc[fi][fj];
+                float* row = static_cast<float*>(Cp) + m * ldc;
+                if (full) {
+                    *reinterpret_cast<f32x4*>(row + n) = v;
+                } else if (m < M) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) row[n + r] = v[r];
+                }
+            }
+        }
+    } else {
+        // Round every accumulator to bf16 first (halves the live registers), then store.
+        u32x2 p[FN][FM];
+#pragma unroll
+        for (int fi = 0; fi < FN; ++fi)
+#pragma unroll
+            for (int fj = 0; fj < FM; ++fj)
+                p[fi][fj] = u32x2{pack_bf16x2(acc[fi][fj][0], acc[fi][fj][1]),
+                                  pack_bf16x2(acc[fi][fj][2], acc[fi][fj][3])};
+#pragma unroll
+        for (int fj = 0; fj < FM; ++fj) {
+            const int64_t m = m_base + 16 * fj + (lane & 15);
+#pragma unroll
+            for (int fi = 0; fi < FN; ++fi) {
+                const int64_t n = n_base + 16 * fi + 4 * (lane >> 4);
+                uint16_t* row = static_cast<uint16_t*>(Cp) + m * ldc;
+                if (full) {
+                    *reinterpret_cast<u32x2*>(row + n) = p[fi][fj];
+                } else if (m < M) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            row[n + r] = static_cast<uint16_t>(p[fi][fj][r >> 1] >> (16 * (r & 1)));
+                }
+            }
+        }
+    }
+}
+
+}  // namespace tmm
+
+namespace tmm {
+
+// As store_acc, for v_mfma_f32_32x32x16_bf16 accumulators: fragment [fi][fj] holds
+// D[n][m] = C[m][n] for a 32 (n) x 32 (m) block; lane l, register r carries
+//     m = m_base + 32*fj + (l % 32),   n = n_base + 32*fi + 8*(r / 4) + 4*(l / 32) + (r % 4),
+// so registers 4q .. 4q+3 are four consecutive n of one C row.
+template <int OUT, int FN, int FM>
+__device__ __forceinline__ void store_acc32(void* Cp, int64_t ldc, int64_t M, int64_t N,
+                                            int64_t m_base, int64_t n_base,
+                                            const f32x16 (&acc)[FN][FM], bool vec_ok) {
+    const int lane = lane_id();
+    const bool full = vec_ok && (m_base + 32 * FM <= M) && (n_base + 32 * FN <= N);
 #pragma unroll
     for (int fj = 0; fj < FM; ++fj) {
-        const int64_t m = m_base + 16 * fj + (lane & 15);
+        const int64_t m = m_base + 32 * fj + (lane & 31);
 #pragma unroll
         for (int fi = 0; fi < FN; ++fi) {
-            const int64_t n = n_base + 16 * fi + 4 * (lane >> 4);
-            const f32x4 v = acc[fi][fj];
-            if (full) {
-                if constexpr (OUT == OUT_F32) {
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(Cp) + m * ldc + n) = v;
-                } else {
-                    u32x2 p = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Cp) + m * ldc + n) = p;
-                }
-            } else if (m < M) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (n + r < N) {
-                        if constexpr (OUT == OUT_F32)
-                            static_cast<float*>(Cp)[m * ldc + n + r] = v[r];
-                        else
-                            static_cast<uint16_t*>(Cp)[m * ldc + n + r] = f32_to_bf16(v[r]);
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n_base + 32 * fi + 8 * q + 4 * (lane >> 5);
+                const f32x4 v = {acc[fi][fj][4 * q], acc[fi][fj][4 * q + 1], acc[fi][fj][4 * q + 2],
+                                 acc[fi][fj][4 * q + 3]};
+                if constexpr (OUT == OUT_F32) {
+                    float* row = static_cast<float*>(Cp) + m * ldc;
+                    if (full) {
+                        *reinterpret_cast<f32x4*>(row + n) = v;
+                    } else if (m < M) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < N) row[n + r] = v[r];
+                    }
+                } else {
+                    uint16_t* row = static_cast<uint16_t*>(Cp) + m * ldc;
+                    const u32x2 p = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    if (full) {
+                        *reinterpret_cast<u32x2*>(row + n) = p;
+                    } else if (m < M) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < N) row[n + r] = static_cast<uint16_t>(p[r >> 1] >> (16 * (r & 1)));
                     }
                 }
             }

@@ -139,6 +139,18 @@ int plan_pipe(const Shape& s, bool persistent, int cus, Plan& p) {
     return GEMM_OK;
 }
 
+// Eight waves, two consumer groups sharing the B tile; always 256 x 256 tiles, persistent.
+int plan_spec(const Shape& s, int cus, Plan& p) {
+    if (!fast_loads_ok(s, 256)) return GEMM_ERR_UNSUPPORTED;
+    tile_grid(s, 256, 256, p);
+    p.kernel = K_SPEC_256;
+    p.grid_x = std::min(p.grid.total, cus);
+    p.grid_y = p.grid_z = 1;
+    p.block = 512;
+    p.vec_store = vec_store_ok(s);
+    return GEMM_OK;
+}
+
 bool gemv_ok(const Shape& s) {
     if (s.M > 16 || s.batch != 1) return false;
     if (!aligned(s.A, 16) || !aligned(s.B, 16) || s.lda % 8 || s.ldb % 8 || s.K % 8) return false;
@@ -173,12 +185,13 @@ int make_plan(int variant, const Shape& s, int cus, Plan& p) {
         case GEMM_VARIANT_MFMA: return plan_2d(s, K_MFMA_128, 128, p);
         case GEMM_VARIANT_PIPELINED: return plan_pipe(s, false, cus, p);
         case GEMM_VARIANT_PERSISTENT: return plan_pipe(s, true, cus, p);
-        case GEMM_VARIANT_SPECIALIZED: return GEMM_ERR_UNSUPPORTED;
+        case GEMM_VARIANT_SPECIALIZED: return plan_spec(s, cus, p);
         case GEMM_VARIANT_GEMV: return plan_gemv(s, p);
         default: break;
     }
     // AUTO
     if (gemv_ok(s)) return plan_gemv(s, p);
+    if (use_big_tile(s, cus) && plan_spec(s, cus, p) == GEMM_OK) return GEMM_OK;
     if (plan_pipe(s, true, cus, p) == GEMM_OK) return GEMM_OK;
     int rc = plan_2d(s, K_MFMA_128, 128, p);
     if (rc == GEMM_OK) return rc;
@@ -210,7 +223,8 @@ int run(int variant, const Shape& s, void* stream) {
         case K_PIPE_256:
         case K_PIPE_128:
         case K_PERSIST_256:
-        case K_PERSIST_128: e = launch_pipe(g, s.out, p, st); break;
+        case K_PERSIST_128:
+        case K_SPEC_256: e = launch_pipe(g, s.out, p, st); break;
         case K_GEMV: e = launch_gemv(g, s.out, p, st); break;
         default: return GEMM_ERR_UNSUPPORTED;
     }

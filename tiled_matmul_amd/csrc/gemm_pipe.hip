@@ -31,17 +31,17 @@
 
 namespace tmm {
 
-template <int BM, int BN, int BK, int STAGES, int SWZ>
+template <int BM, int BN, int BK, int STAGES, int SWZ, int WAVES_M = 2, int WAVES_N = 2>
 struct PipeCfg {
-    static constexpr int WM = BM / 2, WN = BN / 2;      // wave tile (2 x 2 waves)
-    static constexpr int FM = WM / 16, FN = WN / 16;    // 16-wide fragments per wave
+    static constexpr int NW = WAVES_M * WAVES_N;        // waves per workgroup
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
     static constexpr int KC = BK / 8;                   // 16-byte chunks per LDS row
     static constexpr int R = 64 / KC;                   // LDS rows per wave load instruction
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int IA = BM / (4 * R), IB = BN / (4 * R);   // loads per wave per stage
+    static constexpr int IA = BM / (NW * R), IB = BN / (NW * R);   // loads per wave per stage
     static constexpr int LOADS = IA + IB;
-    static_assert(IA * 4 * R == BM && IB * 4 * R == BN, "tile rows must split over 4 waves");
+    static_assert(IA * NW * R == BM && IB * NW * R == BN, "tile rows must split over the waves");
     static_assert(BK % 32 == 0 && KC <= 8, "BK must be 32 or 64");
     static_assert(STAGES >= 2, "at least double buffering");
     static_assert((STAGES - 1) * LOADS <= 63, "vmcnt holds at most 63 outstanding loads");
@@ -60,34 +60,77 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int BK, int STAGES, int SWZ, int OUT, bool XCD_ORDER>
-__global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(GemmArgs g, TileGrid tg, int vec_store) {
-    typedef PipeCfg<BM, BN, BK, STAGES, SWZ> P;
+// The two bf16 MFMA shapes of gfx950.  ROWS x ROWS output block per instruction, KS = k
+// depth per instruction; lane l supplies row (l % ROWS) and the 8-element k chunk
+// (l / ROWS) of each operand.
+template <int MF>
+struct Mma;
+template <>
+struct Mma<16> {
+    static constexpr int ROWS = 16, KS = 32;
+    typedef f32x4 Acc;
+    static __device__ __forceinline__ Acc run(bf16x8 a, bf16x8 b, Acc c) { return mfma_16x16x32(a, b, c); }
+    static __device__ __forceinline__ Acc zero() { return Acc{0.f, 0.f, 0.f, 0.f}; }
+};
+template <>
+struct Mma<32> {
+    static constexpr int ROWS = 32, KS = 16;
+    typedef f32x16 Acc;
+    static __device__ __forceinline__ Acc run(bf16x8 a, bf16x8 b, Acc c) { return mfma_32x32x16(a, b, c); }
+    static __device__ __forceinline__ Acc zero() {
+        Acc z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0.f;
+        return z;
+    }
+};
+
+// Register fragments of one k step of a wave: FN fragments of the B tile (the MFMA's first
+// operand) and FM of the A tile (its second).
+template <int FN, int FM>
+struct Frags {
+    bf16x8 b[FN];
+    bf16x8 a[FM];
+};
+
+template <int BM, int BN, int BK, int STAGES, int SWZ, int MF, int OUT, bool XCD_ORDER, int WAVES_M,
+          int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void gemm_pipe_kernel(
+    GemmArgs g, TileGrid tg, int vec_store) {
+    typedef PipeCfg<BM, BN, BK, STAGES, SWZ, WAVES_M, WAVES_N> P;
+    typedef Mma<MF> T;
+    constexpr int KSTEPS = BK / T::KS;
+    constexpr int FN = P::WN / T::ROWS, FM = P::WM / T::ROWS;   // fragments per wave
     __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * P::STAGE_BYTES];
 
     const int lane = lane_id(), w = wave_id();
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / WAVES_N, wn = w % WAVES_N;
     const int nk = static_cast<int>((g.K + BK - 1) / BK);
+    const uint32_t K = static_cast<uint32_t>(g.K);
+    constexpr int NW = P::NW;
 
-    // Per-lane global offsets (bytes from the tile's first row, at k = 0) of the 16-byte
-    // chunk this lane moves in each of its load instructions, and the matching LDS row
-    // chunk it lands in.  Load i of wave w covers LDS rows [(4 i + w) R, (4 i + w + 1) R).
+    // Per-lane element k offset of the 16-byte chunk this lane moves in each of its load
+    // instructions.  Load i of wave w covers LDS rows [(NW i + w) R, (NW i + w + 1) R); lane
+    // writes physical slot (lane % KC) of row (lane / KC), which holds logical chunk
+    // slot ^ swz(row).
     const int lrow = lane / P::KC, lslot = lane % P::KC;
-    uint32_t chunk_k[P::IA > P::IB ? P::IA : P::IB];    // element k offset of the chunk
+    constexpr int IMAX = P::IA > P::IB ? P::IA : P::IB;
+    uint32_t chunk_k[IMAX];
 #pragma unroll
-    for (int i = 0; i < (P::IA > P::IB ? P::IA : P::IB); ++i) {
-        const int r = (4 * i + w) * P::R + lrow;
+    for (int i = 0; i < IMAX; ++i) {
+        const int r = (NW * i + w) * P::R + lrow;
         chunk_k[i] = 8u * static_cast<uint32_t>(lslot ^ P::swz(r));
     }
-    // Fragment read offsets within a stage (bytes), for each 32-wide k step: row
-    // (lane % 16) of a 16-row block (the swizzle depends on row % 16 only), chunk
-    // 4 kk + lane / 16.
-    int rd[BK / 32];
+    // Fragment read offsets within a stage (bytes), for each k step: row (lane % ROWS) of
+    // a ROWS-row block (the swizzle depends on row % 8 only), chunk
+    // (KS / 8) kk + lane / ROWS.
+    int rd[KSTEPS];
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-        const int r = lane & 15, c = 4 * kk + (lane >> 4);
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int r = lane % T::ROWS, c = (T::KS / 8) * kk + lane / T::ROWS;
         rd[kk] = r * BK * 2 + ((c ^ P::swz(r)) * 16);
     }
+    const int a_frag0 = wm * P::WM * BK * 2, b_frag0 = P::A_BYTES + wn * P::WN * BK * 2;
 
     for (int t = blockIdx.x; t < tg.total; t += gridDim.x) {
         int bt, tm, tn;
@@ -110,104 +153,149 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(GemmArgs g, TileGrid 
         uint32_t va[P::IA], vb[P::IB];
 #pragma unroll
         for (int i = 0; i < P::IA; ++i) {
-            const int r = (4 * i + w) * P::R + lrow;
+            const int r = (NW * i + w) * P::R + lrow;
             va[i] = r < rows_a ? static_cast<uint32_t>(r * g.lda) * 2u + 2u * chunk_k[i] : OOB;
         }
 #pragma unroll
         for (int i = 0; i < P::IB; ++i) {
-            const int r = (4 * i + w) * P::R + lrow;
+            const int r = (NW * i + w) * P::R + lrow;
             vb[i] = r < rows_b ? static_cast<uint32_t>(r * g.ldb) * 2u + 2u * chunk_k[i] : OOB;
         }
 
-        // Issue all loads of K block kb into ring slot `slot`.
+        // Issue every load of K block kb into ring slot `slot`.  Chunks at k >= K (the K
+        // tail) get out-of-range offsets and write zeros.
         auto issue = [&](int kb, int slot) {
             uint8_t* sa = lds + slot * P::STAGE_BYTES;
             uint8_t* sb = sa + P::A_BYTES;
             const uint32_t k0 = static_cast<uint32_t>(kb) * BK;
             const uint32_t soff = 2u * k0;
-            if (k0 + BK <= static_cast<uint32_t>(g.K)) {
+            if (k0 + BK <= K) {
 #pragma unroll
                 for (int i = 0; i < P::IA; ++i)
-                    load_lds_16(ra, sa + (4 * i + w) * P::R * BK * 2, va[i], soff);
+                    load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2, va[i], soff);
 #pragma unroll
                 for (int i = 0; i < P::IB; ++i)
-                    load_lds_16(rb, sb + (4 * i + w) * P::R * BK * 2, vb[i], soff);
-            } else {  // K tail: chunks at k >= K read zeros
+                    load_lds_16(rb, sb + (NW * i + w) * P::R * BK * 2, vb[i], soff);
+            } else {
 #pragma unroll
-                for (int i = 0; i < P::IA; ++i) {
-                    const bool ok = k0 + chunk_k[i] < static_cast<uint32_t>(g.K);
-                    load_lds_16(ra, sa + (4 * i + w) * P::R * BK * 2, ok ? va[i] : OOB, soff);
-                }
+                for (int i = 0; i < P::IA; ++i)
+                    load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2,
+                                k0 + chunk_k[i] < K ? va[i] : OOB, soff);
 #pragma unroll
-                for (int i = 0; i < P::IB; ++i) {
-                    const bool ok = k0 + chunk_k[i] < static_cast<uint32_t>(g.K);
-                    load_lds_16(rb, sb + (4 * i + w) * P::R * BK * 2, ok ? vb[i] : OOB, soff);
-                }
+                for (int i = 0; i < P::IB; ++i)
+                    load_lds_16(rb, sb + (NW * i + w) * P::R * BK * 2,
+                                k0 + chunk_k[i] < K ? vb[i] : OOB, soff);
             }
         };
-
-        f32x4 acc[P::FN][P::FM];
+        auto read_frags = [&](Frags<FN, FM>& f, int slot, int kk) {
+            const uint8_t* base = lds + slot * P::STAGE_BYTES + rd[kk];
 #pragma unroll
-        for (int i = 0; i < P::FN; ++i)
+            for (int i = 0; i < FN; ++i)
+                f.b[i] = *reinterpret_cast<const bf16x8*>(base + b_frag0 + T::ROWS * i * BK * 2);
 #pragma unroll
-            for (int j = 0; j < P::FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < FM; ++j)
+                f.a[j] = *reinterpret_cast<const bf16x8*>(base + a_frag0 + T::ROWS * j * BK * 2);
+        };
 
-        // Prologue: the first STAGES-1 K blocks.  (Every wave has passed the previous
-        // tile's final barrier, so the whole ring is free.)
+        typename T::Acc acc[FN][FM];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = T::zero();
+
+        // Prologue: K blocks 0 .. STAGES-2 into slots 0 .. STAGES-2 (every wave has passed
+        // the previous tile's final barrier, so the whole ring is free).
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
             if (s < nk) issue(s, s);
 
         for (int kb = 0; kb < nk; ++kb) {
-            // Block kb has landed once at most (STAGES-2) later blocks are outstanding.
+            // Block kb has landed once at most STAGES-2 later blocks are outstanding (this
+            // wave's loads); the barrier extends that to every wave's loads, and certifies
+            // that every wave is done reading block kb-1, whose slot is refilled next.
             if (kb + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * P::LOADS>();
             else wait_vmcnt<0>();
-            barrier();  // every wave's share of block kb is in LDS; block kb-1 is consumed
+            barrier();
             if (kb + STAGES - 1 < nk) issue(kb + STAGES - 1, (kb + STAGES - 1) % STAGES);
 
-            const uint8_t* sa = lds + (kb % STAGES) * P::STAGE_BYTES;
-            const uint8_t* sb = sa + P::A_BYTES;
+            // The k steps of block kb: the fragments of step kk+1 are read from LDS while
+            // the MFMAs of step kk run (iglp_opt(0) interleaves the two streams).
+            const int slot = kb % STAGES;
+            Frags<FN, FM> f[2];
+            read_frags(f[0], slot, 0);
 #pragma unroll
-            for (int kk = 0; kk < BK / 32; ++kk) {
-                bf16x8 fb[P::FN], fa[P::FM];
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                if (kk + 1 < KSTEPS) read_frags(f[(kk + 1) & 1], slot, kk + 1);
 #pragma unroll
-                for (int i = 0; i < P::FN; ++i)
-                    fb[i] = *reinterpret_cast<const bf16x8*>(sb + (wn * P::WN + 16 * i) * BK * 2 + rd[kk]);
+                for (int i = 0; i < FN; ++i)
 #pragma unroll
-                for (int j = 0; j < P::FM; ++j)
-                    fa[j] = *reinterpret_cast<const bf16x8*>(sa + (wm * P::WM + 16 * j) * BK * 2 + rd[kk]);
-#pragma unroll
-                for (int i = 0; i < P::FN; ++i)
-#pragma unroll
-                    for (int j = 0; j < P::FM; ++j) acc[i][j] = mfma_16x16x32(fb[i], fa[j], acc[i][j]);
+                    for (int j = 0; j < FM; ++j) acc[i][j] = T::run(f[kk & 1].b[i], f[kk & 1].a[j], acc[i][j]);
+                __builtin_amdgcn_iglp_opt(0);
             }
         }
         barrier();  // all fragment reads of this tile are done before the ring is refilled
 
         void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
                                   : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
-        store_acc<OUT, P::FN, P::FM>(Cb, g.ldc, g.M, g.N, m0 + wm * P::WM, n0 + wn * P::WN, acc,
+        if constexpr (MF == 16)
+            store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * P::WM, n0 + wn * P::WN, acc,
+                                   vec_store != 0);
+        else
+            store_acc32<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * P::WM, n0 + wn * P::WN, acc,
                                      vec_store != 0);
     }
 }
 
-template <int BM, int BN, int BK, int STAGES, int SWZ, bool XCD>
+// MFMA shape of the 4-wave and of the 8-wave kernels (16 = v_mfma_f32_16x16x32_bf16,
+// 32 = v_mfma_f32_32x32x16_bf16); 16 measured faster for both on MI355X.
+#ifndef TMM_MFMA
+#define TMM_MFMA 16
+#endif
+
+#ifndef TMM_SPEC_MFMA
+#define TMM_SPEC_MFMA 16
+#endif
+
+template <int BM, int BN, int BK, int STAGES, int SWZ, bool XCD, int MF = TMM_MFMA, int WM = 2, int WN = 2>
 static hipError_t launch_pipe_cfg(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
+    constexpr int THREADS = 64 * WM * WN;
     if (out == OUT_F32)
-        hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, BK, STAGES, SWZ, OUT_F32, XCD>), dim3(p.grid_x),
-                           dim3(256), 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, BK, STAGES, SWZ, MF, OUT_F32, XCD, WM, WN>),
+                           dim3(p.grid_x), dim3(THREADS), 0, s, g, p.grid, p.vec_store);
     else
-        hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, BK, STAGES, SWZ, OUT_BF16, XCD>), dim3(p.grid_x),
-                           dim3(256), 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, BK, STAGES, SWZ, MF, OUT_BF16, XCD, WM, WN>),
+                           dim3(p.grid_x), dim3(THREADS), 0, s, g, p.grid, p.vec_store);
     return hipGetLastError();
 }
 
+// Ring shape of the two tile sizes: K block, ring depth, swizzle pattern.
+#ifndef TMM_BIG_BK
+#define TMM_BIG_BK 64
+#endif
+#ifndef TMM_BIG_STAGES
+#define TMM_BIG_STAGES 2
+#endif
+#ifndef TMM_SMALL_BK
+#define TMM_SMALL_BK 64
+#endif
+#ifndef TMM_SMALL_STAGES
+#define TMM_SMALL_STAGES 3
+#endif
+#ifndef TMM_SWZ
+#define TMM_SWZ 1
+#endif
+
 hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
+    constexpr int BBK = TMM_BIG_BK, BST = TMM_BIG_STAGES, SBK = TMM_SMALL_BK, SST = TMM_SMALL_STAGES;
+    constexpr int SWZ = TMM_SWZ;
     switch (p.kernel) {
-        case K_PIPE_256: return launch_pipe_cfg<256, 256, 64, 2, 1, false>(g, out, p, s);
-        case K_PIPE_128: return launch_pipe_cfg<128, 128, 64, 3, 1, false>(g, out, p, s);
-        case K_PERSIST_256: return launch_pipe_cfg<256, 256, 64, 2, 1, true>(g, out, p, s);
-        case K_PERSIST_128: return launch_pipe_cfg<128, 128, 64, 3, 1, true>(g, out, p, s);
+        case K_PIPE_256: return launch_pipe_cfg<256, 256, BBK, BST, SWZ, false>(g, out, p, s);
+        case K_PIPE_128: return launch_pipe_cfg<128, 128, SBK, SST, SWZ, false>(g, out, p, s);
+        case K_PERSIST_256: return launch_pipe_cfg<256, 256, BBK, BST, SWZ, true>(g, out, p, s);
+        case K_PERSIST_128: return launch_pipe_cfg<128, 128, SBK, SST, SWZ, true>(g, out, p, s);
+        // Two consumer groups of four waves (rows 0-127 and 128-255) share each B stage.
+        case K_SPEC_256:
+            return launch_pipe_cfg<256, 256, BBK, BST, SWZ, true, TMM_SPEC_MFMA, 2, 4>(g, out, p, s);
         default: return hipErrorInvalidValue;
     }
 }

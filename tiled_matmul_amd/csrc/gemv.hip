@@ -20,6 +20,11 @@
 
 namespace tmm {
 
+// Cache policy bits of the W loads (W is streamed once).
+#ifndef TMM_GEMV_AUX
+#define TMM_GEMV_AUX 0
+#endif
+
 template <int OUT, int UNROLL>
 __global__ __launch_bounds__(512) void gemv_kernel(GemmArgs g) {
     constexpr int WAVES = 8;
@@ -45,7 +50,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemmArgs g) {
             const int s = s0 + u * WAVES;
             const uint32_t k = static_cast<uint32_t>(s) * 32u + 8u * c;   // this lane's chunk
             const bool ok = s < steps && k < K;
-            wv[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? vw : OOB, 64u * s, 0);
+            wv[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? vw : OOB, 64u * s, TMM_GEMV_AUX);
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
@@ -83,11 +88,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemmArgs g) {
     }
 }
 
+#ifndef TMM_GEMV_UNROLL
+#define TMM_GEMV_UNROLL 8
+#endif
+
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
+    constexpr int U = TMM_GEMV_UNROLL;
     if (out == OUT_F32)
-        hipLaunchKernelGGL((gemv_kernel<OUT_F32, 8>), dim3(p.grid_x), dim3(512), 0, s, g);
+        hipLaunchKernelGGL((gemv_kernel<OUT_F32, U>), dim3(p.grid_x), dim3(512), 0, s, g);
     else
-        hipLaunchKernelGGL((gemv_kernel<OUT_BF16, 8>), dim3(p.grid_x), dim3(512), 0, s, g);
+        hipLaunchKernelGGL((gemv_kernel<OUT_BF16, U>), dim3(p.grid_x), dim3(512), 0, s, g);
     return hipGetLastError();
 }
 
