@@ -70,7 +70,9 @@ def plan(variant=0, batch=1, M=4096, N=4096, K=4096, A=P, lda=None, sA=0, B=P, l
 
 def test_plan_workloads():
     assert plan()[:2] == (0, "spec_256")
-    assert plan(M=1)[:2] == (0, "gemv")
+    assert plan(M=1)[:2] == (0, "gemv_dot")
+    assert plan(M=8)[:2] == (0, "gemv_dot")
+    assert plan(M=9)[:2] == (0, "gemv")
     assert plan(M=16)[:2] == (0, "gemv")
     assert plan(M=17)[1] != "gemv"
     assert plan(M=8192, N=14336, K=4096, out=1)[:2] == (0, "spec_256")

@@ -157,12 +157,19 @@ bool gemv_ok(const Shape& s) {
     return 16 * s.lda * 2 < k2G && 16 * s.ldb * 2 < k2G && cdiv(s.N, 16) < k2G;
 }
 
+// M <= 8: the dot-product form; 8 < M <= 16: the MFMA form.
 int plan_gemv(const Shape& s, Plan& p) {
     if (!gemv_ok(s)) return GEMM_ERR_UNSUPPORTED;
-    p.kernel = K_GEMV;
-    p.grid_x = static_cast<int>(cdiv(s.N, 16));
+    if (s.M <= 8) {
+        p.kernel = K_GEMV_DOT;
+        p.grid_x = static_cast<int>(cdiv(s.N, gemv_dot_rows_per_workgroup()));
+        p.block = 256;
+    } else {
+        p.kernel = K_GEMV;
+        p.grid_x = static_cast<int>(cdiv(s.N, 16));
+        p.block = 512;
+    }
     p.grid_y = p.grid_z = 1;
-    p.block = 512;
     return GEMM_OK;
 }
 
@@ -226,6 +233,7 @@ int run(int variant, const Shape& s, void* stream) {
         case K_PERSIST_128:
         case K_SPEC_256: e = launch_pipe(g, s.out, p, st); break;
         case K_GEMV: e = launch_gemv(g, s.out, p, st); break;
+        case K_GEMV_DOT: e = launch_gemv_dot(g, s.out, p, st); break;
         default: return GEMM_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
@@ -294,6 +302,7 @@ const char* gemm_bf16_kernel_name(int k) {
         case K_PERSIST_128: return "persist_128";
         case K_SPEC_256: return "spec_256";
         case K_GEMV: return "gemv";
+        case K_GEMV_DOT: return "gemv_dot";
         default: return "?";
     }
 }

@@ -19,8 +19,9 @@ enum KernelId {
     K_PERSIST_256 = 6,      // ladder step 4: persistent, XCD-aware grouped order, 256x256
     K_PERSIST_128 = 7,      //   same, 128x128
     K_SPEC_256 = 8,         // ladder step 5: wave-specialised, two consumer groups share B
-    K_GEMV = 9,             // ladder step 6: skinny-M bandwidth path
-    K_COUNT = 10
+    K_GEMV = 9,             // ladder step 6: skinny-M bandwidth path, MFMA form (M <= 16)
+    K_GEMV_DOT = 10,        //   same, dot-product form with contiguous loads (M <= 8)
+    K_COUNT = 11
 };
 
 // Launch shape chosen for a problem (filled by the planner, consumed by the launchers).
@@ -38,5 +39,7 @@ hipError_t launch_mfma(const GemmArgs& g, int out, const Plan& p, hipStream_t s)
 hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_spec(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_gemv_dot(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+int gemv_dot_rows_per_workgroup();
 
 }  // namespace tmm

@@ -1,0 +1,86 @@
+"""Summaries of rocprofv3 output for the committed profiles (host tool, no GPU).
+
+    python -m tiled_matmul_amd.proftools stats <kernel_stats.csv | kernel_trace.csv>
+        per-kernel dispatch count and average / min / max duration (us)
+    python -m tiled_matmul_amd.proftools traffic --fetch F.csv --write W.csv \
+        --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --kernel SUBSTR \
+        --workload NAME --sha SHA --out profiles/traffic_<kernel>_<workload>.json
+        HBM bytes per launch of the kernel whose name contains SUBSTR, from FETCH_SIZE and
+        WRITE_SIZE counter runs (KiB per dispatch), each scaled by the ratio of the known size
+        of a plain copy kernel to what the same counter read for it.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import statistics
+from collections import defaultdict
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def kernel_durations(path):
+    """{kernel name: [duration ns, ...]} from a kernel trace CSV."""
+    d = defaultdict(list)
+    for r in _rows(path):
+        name = r.get("Kernel_Name") or r.get("Name")
+        if "Start_Timestamp" in r and "End_Timestamp" in r:
+            d[name].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return d
+
+
+def counter_per_dispatch(path, counter, substr):
+    """Average over dispatches of `counter` for kernels whose name contains substr."""
+    per = defaultdict(float)
+    for r in _rows(path):
+        if r["Counter_Name"] == counter and substr in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for a kernel containing {substr!r} in {path}")
+    return statistics.mean(per.values()), len(per)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("trace")
+    t = sub.add_parser("traffic")
+    for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--workload",
+              "--sha", "--out"):
+        t.add_argument(a, required=True)
+    t.add_argument("--copy-kernel", default="copy")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    a = ap.parse_args()
+    if a.cmd == "stats":
+        for name, v in sorted(kernel_durations(a.trace).items(), key=lambda x: -sum(x[1])):
+            print(f"| {name[:90]} | {len(v)} | {statistics.mean(v) / 1e3:.2f} | "
+                  f"{min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} |")
+        return
+    fetch, nf = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
+    write, nw = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    cfetch, _ = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
+    cwrite, _ = counter_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel)
+    f_scale = a.copy_bytes / (cfetch * 1024.0)
+    w_scale = a.copy_bytes / (cwrite * 1024.0)
+    out = {
+        "kernel": a.kernel, "workload": a.workload, "kernel_source_sha": a.sha,
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+        "dispatches": [nf, nw],
+        "copy_calibration": {"bytes": a.copy_bytes, "fetch_kib": cfetch, "write_kib": cwrite,
+                             "fetch_scale": f_scale, "write_scale": w_scale},
+        "hbm_read_bytes_per_launch": fetch * 1024.0 * f_scale,
+        "hbm_write_bytes_per_launch": write * 1024.0 * w_scale,
+    }
+    out["hbm_bytes_per_launch"] = out["hbm_read_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
+    with open(a.out, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+if __name__ == "__main__":
+    main()
