@@ -62,6 +62,7 @@ extern "C" {
 #define GEMM_VARIANT_PERSISTENT 4  /* step 6: + persistent workgroups, XCD-aware tile order    */
 #define GEMM_VARIANT_SPECIALIZED 5 /* steps 7-9: producer/consumer waves sharing the B tile    */
 #define GEMM_VARIANT_GEMV 6        /* skinny M (M <= 16): bandwidth-bound decode path         */
+#define GEMM_VARIANT_PINGPONG 7    /* steps 7-9: two wave groups alternate load / MFMA phases  */
 
 /*
  * C = A * B^T for one problem (definition above).

@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tm.gemm_bf16_version() == 1
+    assert tm.gemm_bf16_version() == 2
     for s in range(7):
         assert tm.gemm_bf16_status_string(s).startswith("GEMM_")
     assert tm.gemm_bf16_status_string(99) == "unknown status"
@@ -97,7 +97,8 @@ def test_plan_variant_preconditions():
     assert plan(variant=6, M=17)[0] == tm.GEMM_ERR_UNSUPPORTED
     assert plan(variant=3, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
     assert plan(variant=4, A=P + 2)[0] == tm.GEMM_ERR_UNSUPPORTED
-    assert plan(variant=7)[0] == tm.GEMM_ERR_ARG
+    assert plan(variant=8)[0] == tm.GEMM_ERR_ARG
+    assert plan(variant=7)[:2] == (0, "pingpong_256")
     assert plan(variant=5, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
     assert plan(variant=1)[1] == "simple_64"
     assert plan(variant=2)[1] == "mfma_128"

@@ -39,11 +39,13 @@ GEMM_VARIANT_PIPELINED = 3
 GEMM_VARIANT_PERSISTENT = 4
 GEMM_VARIANT_SPECIALIZED = 5
 GEMM_VARIANT_GEMV = 6
+GEMM_VARIANT_PINGPONG = 7
 
 VARIANTS = {
     "auto": GEMM_VARIANT_AUTO, "simple": GEMM_VARIANT_SIMPLE, "mfma": GEMM_VARIANT_MFMA,
     "pipelined": GEMM_VARIANT_PIPELINED, "persistent": GEMM_VARIANT_PERSISTENT,
     "specialized": GEMM_VARIANT_SPECIALIZED, "gemv": GEMM_VARIANT_GEMV,
+    "pingpong": GEMM_VARIANT_PINGPONG,
 }
 
 

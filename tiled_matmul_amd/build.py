@@ -22,10 +22,16 @@ CFLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Per-file compiler options.  The pipelined GEMM keeps MFMA fragments live across its K-block
+# loop; LLVM's default scheduler then over-commits VGPRs and shuffles accumulators through
+# AGPR copies, which the iterative ILP scheduler avoids.
+FILE_FLAGS = {"gemm_pipe.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+
+
 def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-I", os.path.dirname(src), *[f"-D{d}" for d in defines], "-c", src,
-           "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-I", os.path.dirname(src),
+           *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

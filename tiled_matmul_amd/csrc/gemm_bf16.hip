@@ -11,7 +11,7 @@ using namespace tmm;
 
 namespace {
 
-constexpr int kVersion = 1;
+constexpr int kVersion = 2;
 constexpr int kDefaultCUs = 256;        // MI355X
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t k2G = int64_t(1) << 31;
@@ -140,10 +140,12 @@ int plan_pipe(const Shape& s, bool persistent, int cus, Plan& p) {
 }
 
 // Eight waves, two consumer groups sharing the B tile; always 256 x 256 tiles, persistent.
-int plan_spec(const Shape& s, int cus, Plan& p) {
+// `kernel`: K_SPEC_256 (both groups load and multiply in lockstep) or K_PINGPONG_256 (the
+// groups alternate load and MFMA phases).
+int plan_spec(const Shape& s, int cus, Plan& p, int kernel = K_SPEC_256) {
     if (!fast_loads_ok(s, 256)) return GEMM_ERR_UNSUPPORTED;
     tile_grid(s, 256, 256, p);
-    p.kernel = K_SPEC_256;
+    p.kernel = kernel;
     p.grid_x = std::min(p.grid.total, cus);
     p.grid_y = p.grid_z = 1;
     p.block = 512;
@@ -174,7 +176,7 @@ int plan_gemv(const Shape& s, Plan& p) {
 }
 
 int make_plan(int variant, const Shape& s, int cus, Plan& p) {
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_GEMV) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_PINGPONG) return GEMM_ERR_ARG;
     p = Plan{};
     if (s.batch == 0 || s.M == 0 || s.N == 0) {
         p.kernel = K_NONE;
@@ -194,6 +196,7 @@ int make_plan(int variant, const Shape& s, int cus, Plan& p) {
         case GEMM_VARIANT_PERSISTENT: return plan_pipe(s, true, cus, p);
         case GEMM_VARIANT_SPECIALIZED: return plan_spec(s, cus, p);
         case GEMM_VARIANT_GEMV: return plan_gemv(s, p);
+        case GEMM_VARIANT_PINGPONG: return plan_spec(s, cus, p, K_PINGPONG_256);
         default: break;
     }
     // AUTO
@@ -208,7 +211,7 @@ int make_plan(int variant, const Shape& s, int cus, Plan& p) {
 int run(int variant, const Shape& s, void* stream) {
     int rc = validate(s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC, s.out);
     if (rc != GEMM_OK) return rc;
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_GEMV) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_PINGPONG) return GEMM_ERR_ARG;
     if (s.batch == 0 || s.M == 0 || s.N == 0) return GEMM_OK;
     int cus = 0;
     rc = current_device(&cus);
@@ -232,6 +235,7 @@ int run(int variant, const Shape& s, void* stream) {
         case K_PERSIST_256:
         case K_PERSIST_128:
         case K_SPEC_256: e = launch_pipe(g, s.out, p, st); break;
+        case K_PINGPONG_256: e = launch_pingpong(g, s.out, p, st); break;
         case K_GEMV: e = launch_gemv(g, s.out, p, st); break;
         case K_GEMV_DOT: e = launch_gemv_dot(g, s.out, p, st); break;
         default: return GEMM_ERR_UNSUPPORTED;
@@ -301,6 +305,7 @@ const char* gemm_bf16_kernel_name(int k) {
         case K_PERSIST_256: return "persist_256";
         case K_PERSIST_128: return "persist_128";
         case K_SPEC_256: return "spec_256";
+        case K_PINGPONG_256: return "pingpong_256";
         case K_GEMV: return "gemv";
         case K_GEMV_DOT: return "gemv_dot";
         default: return "?";

@@ -54,10 +54,19 @@ struct PipeCfg {
     }
 };
 
+// s_waitcnt through the builtin, so that the compiler's own wait insertion sees it.  gfx9
+// encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]; an all-ones field
+// does not wait on that counter.
+template <int VM, int LGKM = 15>
+__device__ __forceinline__ void wait_cnt() {
+    static_assert(VM >= 0 && VM <= 63 && LGKM >= 0 && LGKM <= 15, "counter range");
+    constexpr int enc = (VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14);
+    __builtin_amdgcn_s_waitcnt(enc);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    wait_cnt<N, 15>();
 }
 
 // The two bf16 MFMA shapes of gfx950.  ROWS x ROWS output block per instruction, KS = k
@@ -85,6 +94,46 @@ struct Mma<32> {
     }
 };
 
+// One k step of MFMAs on fragments `f`, with NR fragment reads (rd(q)) and NG load issues
+// (ld(q)) for later steps placed evenly between groups of MFMAs.  sched_barrier fences fix
+// this order: LDS reads issued in one burst fill the LDS command FIFO and, since a wave
+// issues in order, stall the MFMAs queued behind them.
+// FINE = false keeps the reads and loads in one group ahead of the MFMAs (the 4-wave kernel,
+// whose 256 accumulators leave LLVM too few registers to interleave without copies).
+template <int FN, int FM, int NR, int NG, bool FINE, typename Acc, typename F, typename RD, typename LD>
+__device__ __forceinline__ void step(Acc (&acc)[FN][FM], const F& f, RD rd, LD ld) {
+    constexpr int NM = FN * FM;
+    if constexpr (!FINE) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) rd(q);
+#pragma unroll
+        for (int q = 0; q < NG; ++q) ld(q);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[m / FM][m % FM] = Mma<(sizeof(Acc) == 16 ? 16 : 32)>::run(
+            f.b[m / FM], f.a[m % FM], acc[m / FM][m % FM]);
+        __builtin_amdgcn_sched_barrier(0);
+        return;
+    }
+    constexpr int SLOTS = NR > NG ? NR : NG;
+    static_assert(!FINE || NM >= SLOTS, "needs at least one MFMA per slot");
+#pragma unroll
+    for (int q = 0; q < SLOTS; ++q) {
+        if (q < NR) rd(q);
+        if (q < NG) ld(q);
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int base = NM / SLOTS, extra = NM % SLOTS;
+        const int m0 = q * base + (q < extra ? q : extra);
+        const int m1 = m0 + base + (q < extra ? 1 : 0);
+#pragma unroll
+        for (int m = m0; m < m1; ++m) {
+            const int i = m / FM, j = m % FM;
+            acc[i][j] = Mma<(sizeof(Acc) == 16 ? 16 : 32)>::run(f.b[i], f.a[j], acc[i][j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Register fragments of one k step of a wave: FN fragments of the B tile (the MFMA's first
 // operand) and FM of the A tile (its second).
 template <int FN, int FM>
@@ -93,6 +142,10 @@ struct Frags {
     bf16x8 a[FM];
 };
 
+#ifndef TMM_PREFETCH
+#define TMM_PREFETCH 0
+#endif
+
 template <int BM, int BN, int BK, int STAGES, int SWZ, int MF, int OUT, bool XCD_ORDER, int WAVES_M,
           int WAVES_N>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void gemm_pipe_kernel(
@@ -100,8 +153,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     typedef PipeCfg<BM, BN, BK, STAGES, SWZ, WAVES_M, WAVES_N> P;
     typedef Mma<MF> T;
     constexpr int KSTEPS = BK / T::KS;
+    constexpr bool FINE = WAVES_M * WAVES_N >= 8;   // see step()
     constexpr int FN = P::WN / T::ROWS, FM = P::WM / T::ROWS;   // fragments per wave
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * P::STAGE_BYTES];
+    // L2 prefetch: with PF > 0, each block's loads are followed by a touch of every
+    // 128-byte row segment of block kb + PF, so that block's own loads find their lines in L2
+    // (the first touch of a cold operand otherwise puts HBM latency inside a ring only
+    // STAGES - 1 blocks deep).  One dword per line, PFN instructions per wave per block,
+    // landing in a 256-byte LDS sink per wave that nothing reads.
+    constexpr int PF = TMM_PREFETCH;
+    constexpr int PFN = PF > 0 ? (BM + BN + 64 * P::NW - 1) / (64 * P::NW) : 0;
+    // Loads issued after the last load of block kb + 1 when block kb + 1 must have landed.
+    constexpr int WAIT_N = (STAGES - 2) * P::LOADS + (STAGES - 1) * PFN;
+    static_assert(WAIT_N <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * P::STAGE_BYTES + (PF > 0 ? 256 * P::NW : 0)];
 
     const int lane = lane_id(), w = wave_id();
     const int wm = w / WAVES_N, wn = w % WAVES_N;
@@ -163,29 +227,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         }
 
         // Issue every load of K block kb into ring slot `slot`.  Chunks at k >= K (the K
-        // tail) get out-of-range offsets and write zeros.
+        // tail, or a block past the end) get out-of-range offsets and write zeros.
         auto issue = [&](int kb, int slot) {
             uint8_t* sa = lds + slot * P::STAGE_BYTES;
             uint8_t* sb = sa + P::A_BYTES;
             const uint32_t k0 = static_cast<uint32_t>(kb) * BK;
             const uint32_t soff = 2u * k0;
-            if (k0 + BK <= K) {
 #pragma unroll
-                for (int i = 0; i < P::IA; ++i)
-                    load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2, va[i], soff);
+            for (int i = 0; i < P::IA; ++i)
+                load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2, k0 + chunk_k[i] < K ? va[i] : OOB, soff);
 #pragma unroll
-                for (int i = 0; i < P::IB; ++i)
-                    load_lds_16(rb, sb + (NW * i + w) * P::R * BK * 2, vb[i], soff);
-            } else {
-#pragma unroll
-                for (int i = 0; i < P::IA; ++i)
-                    load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2,
-                                k0 + chunk_k[i] < K ? va[i] : OOB, soff);
-#pragma unroll
-                for (int i = 0; i < P::IB; ++i)
-                    load_lds_16(rb, sb + (NW * i + w) * P::R * BK * 2,
-                                k0 + chunk_k[i] < K ? vb[i] : OOB, soff);
-            }
+            for (int i = 0; i < P::IB; ++i)
+                load_lds_16(rb, sb + (NW * i + w) * P::R * BK * 2, k0 + chunk_k[i] < K ? vb[i] : OOB, soff);
         };
         auto read_frags = [&](Frags<FN, FM>& f, int slot, int kk) {
             const uint8_t* base = lds + slot * P::STAGE_BYTES + rd[kk];
@@ -197,42 +250,100 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
                 f.a[j] = *reinterpret_cast<const bf16x8*>(base + a_frag0 + T::ROWS * j * BK * 2);
         };
 
+        // One load instruction of block kb (i < IA: A rows, else B rows) into slot `slot`.
+        auto issue_one = [&](int i, int kb, int slot) {
+            uint8_t* sa = lds + slot * P::STAGE_BYTES;
+            const uint32_t k0 = static_cast<uint32_t>(kb) * BK;
+            if (i < P::IA)
+                load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2, k0 + chunk_k[i] < K ? va[i] : OOB, 2u * k0);
+            else
+                load_lds_16(rb, sa + P::A_BYTES + (NW * (i - P::IA) + w) * P::R * BK * 2,
+                            k0 + chunk_k[i - P::IA] < K ? vb[i - P::IA] : OOB, 2u * k0);
+        };
+        // L2 prefetch of block kb: lane l of wave w, instruction p covers tile row
+        // (p NW + w) 64 + l (A rows first, then B rows).
+        auto prefetch = [&](int kb) {
+            if constexpr (PF > 0) {
+                const uint32_t k0 = static_cast<uint32_t>(kb) * BK;
+#pragma unroll
+                for (int p = 0; p < PFN; ++p) {
+                    const int r = (p * P::NW + w) * 64 + lane;
+                    uint32_t off = OOB;
+                    if (k0 < K) {
+                        if (r < BM) off = r < rows_a ? static_cast<uint32_t>(r * g.lda) * 2u : OOB;
+                        else if (r < BM + BN) off = r - BM < rows_b ? static_cast<uint32_t>((r - BM) * g.ldb) * 2u : OOB;
+                    }
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r < BM ? ra : rb, (lds_ptr_t)(lds + STAGES * P::STAGE_BYTES + 256 * w),
+                                                             4, off, 2u * k0, 0, 0);
+                }
+            }
+        };
+        // One fragment (q < FN: B fragment q, else A fragment q - FN) of k step kk of `slot`.
+        auto read_one = [&](Frags<FN, FM>& f, int q, int slot, int kk) {
+            const uint8_t* base = lds + slot * P::STAGE_BYTES + rd[kk];
+            if (q < FN)
+                f.b[q] = *reinterpret_cast<const bf16x8*>(base + b_frag0 + T::ROWS * q * BK * 2);
+            else
+                f.a[q - FN] = *reinterpret_cast<const bf16x8*>(base + a_frag0 + T::ROWS * (q - FN) * BK * 2);
+        };
+
         typename T::Acc acc[FN][FM];
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j) acc[i][j] = T::zero();
 
-        // Prologue: K blocks 0 .. STAGES-2 into slots 0 .. STAGES-2 (every wave has passed
-        // the previous tile's final barrier, so the whole ring is free).
+        // Prologue: blocks 0 .. STAGES-2, wait for block 0, then block STAGES-1, and the
+        // fragments of block 0's first k step.  (Every wave has passed the previous tile's
+        // final barrier, so the whole ring is free.)
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < nk) issue(s, s);
-
-        for (int kb = 0; kb < nk; ++kb) {
-            // Block kb has landed once at most STAGES-2 later blocks are outstanding (this
-            // wave's loads); the barrier extends that to every wave's loads, and certifies
-            // that every wave is done reading block kb-1, whose slot is refilled next.
-            if (kb + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * P::LOADS>();
-            else wait_vmcnt<0>();
-            barrier();
-            if (kb + STAGES - 1 < nk) issue(kb + STAGES - 1, (kb + STAGES - 1) % STAGES);
-
-            // The k steps of block kb: the fragments of step kk+1 are read from LDS while
-            // the MFMAs of step kk run (iglp_opt(0) interleaves the two streams).
-            const int slot = kb % STAGES;
-            Frags<FN, FM> f[2];
-            read_frags(f[0], slot, 0);
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                if (kk + 1 < KSTEPS) read_frags(f[(kk + 1) & 1], slot, kk + 1);
-#pragma unroll
-                for (int i = 0; i < FN; ++i)
-#pragma unroll
-                    for (int j = 0; j < FM; ++j) acc[i][j] = T::run(f[kk & 1].b[i], f[kk & 1].a[j], acc[i][j]);
-                __builtin_amdgcn_iglp_opt(0);
-            }
+        for (int s = 0; s < STAGES - 1; ++s) {
+            issue(s, s);
+            prefetch(s + PF);
         }
+        wait_vmcnt<WAIT_N>();
+        barrier();
+        issue(STAGES - 1, STAGES - 1);
+        prefetch(STAGES - 1 + PF);
+        Frags<FN, FM> f[2];
+        read_frags(f[0], 0, 0);
+        wait_cnt<63, 0>();
+
+        // Block kb: k steps 0 .. KSTEPS-2 read the next step's fragments, then run their own
+        // MFMAs.  The last step first waits for this wave's loads of block kb+1 and for its
+        // own fragment reads, passes the barrier (every wave's share of kb+1 is in LDS and
+        // every wave is done reading block kb), starts reading block kb+1's first fragments,
+        // refills block kb's slot with block kb+STAGES, and only then runs its MFMAs, so the
+        // reads and loads overlap them.  Blocks past the end are issued too (their chunks
+        // are all beyond K and read as zeros): the count of outstanding loads is then the same
+        // in every iteration and the loop body has no branch.
+        int slot = 0;
+        for (int kb = 0; kb < nk; ++kb) {
+#pragma unroll
+            for (int kk = 0; kk + 1 < KSTEPS; ++kk)
+                step<FN, FM, FN + FM, 0, FINE>(acc, f[kk & 1], [&](int q) { read_one(f[(kk + 1) & 1], q, slot, kk + 1); },
+                                         [&](int) {});
+            constexpr int LAST = (KSTEPS - 1) & 1;
+            const int next_slot = slot + 1 == STAGES ? 0 : slot + 1;
+            wait_cnt<WAIT_N, 0>();
+            barrier();
+            step<FN, FM, FN + FM, P::LOADS, FINE>(acc, f[LAST], [&](int q) { read_one(f[LAST ^ 1], q, next_slot, 0); },
+                                            [&](int q) { issue_one(q, kb + STAGES, slot); });
+            prefetch(kb + STAGES + PF);
+            // The reads of block kb+1's first fragments were interleaved with the MFMAs just
+            // issued and have long completed; saying so here keeps the compiler from stalling
+            // the next iteration's first MFMA on a conservative lgkmcnt.
+            __builtin_amdgcn_sched_barrier(0);
+            wait_cnt<63, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (LAST == 1) {
+                // KSTEPS even: the next block's first fragments went to f[0]; nothing to move.
+            } else {
+                f[0] = f[1];
+            }
+            slot = next_slot;
+        }
+        wait_vmcnt<0>();   // the trailing zero-fill loads have landed
         barrier();  // all fragment reads of this tile are done before the ring is refilled
 
         void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)

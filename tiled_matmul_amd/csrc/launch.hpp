@@ -21,7 +21,8 @@ enum KernelId {
     K_SPEC_256 = 8,         // ladder step 5: wave-specialised, two consumer groups share B
     K_GEMV = 9,             // ladder step 6: skinny-M bandwidth path, MFMA form (M <= 16)
     K_GEMV_DOT = 10,        //   same, dot-product form with contiguous loads (M <= 8)
-    K_COUNT = 11
+    K_PINGPONG_256 = 11,    // ladder steps 7-9: two wave groups alternate load and MFMA phases
+    K_COUNT = 12
 };
 
 // Launch shape chosen for a problem (filled by the planner, consumed by the launchers).
@@ -37,7 +38,7 @@ hipError_t launch_zero_fill(const GemmArgs& g, int out, const Plan& p, hipStream
 hipError_t launch_simple(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_mfma(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
-hipError_t launch_spec(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_pingpong(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_gemv_dot(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 int gemv_dot_rows_per_workgroup();
