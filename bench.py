@@ -61,19 +61,27 @@ def to_dev(bits, torch):
 
 
 def make_sets(name, torch, min_bytes):
-    """Enough copies of the workload's operands (and outputs) to exceed min_bytes."""
+    """Enough copies of the workload's operands (and outputs) to exceed min_bytes.  Device
+    operands are (M, K) and (N, K), or (batch, M, K) and (batch, N, K) for a batched
+    workload; the host arrays returned are batch item 0's."""
     w = synth.WORKLOADS[name]
-    M, N, K, out = w["M"], w["N"], w["K"], w["out"]
-    A, B = synth.make_operands(name)
-    Ad, Bd = to_dev(A, torch), to_dev(B, torch)
+    M, N, K, out, batch = w["M"], w["N"], w["K"], w["out"], w["batch"]
+    items = [synth.make_operands(name, item=b) for b in range(batch)]
+    A, B = items[0]
+    if batch == 1:
+        Ad, Bd = to_dev(A, torch), to_dev(B, torch)
+    else:
+        Ad = to_dev(np.stack([a for a, _ in items]), torch)
+        Bd = to_dev(np.stack([b for _, b in items]), torch)
     out_t = torch.float32 if out == tm.GEMM_OUT_FP32 else torch.bfloat16
-    per = Ad.numel() * 2 + Bd.numel() * 2 + M * N * (4 if out == tm.GEMM_OUT_FP32 else 2)
+    cshape = (M, N) if batch == 1 else (batch, M, N)
+    per = Ad.numel() * 2 + Bd.numel() * 2 + batch * M * N * (4 if out == tm.GEMM_OUT_FP32 else 2)
     n = max(1, -(-min_bytes // per))
     sets = []
     for i in range(n):
         a = Ad if i == 0 else Ad.clone()
         b = Bd if i == 0 else Bd.clone()
-        sets.append((a, b, torch.empty((M, N), dtype=out_t, device="cuda")))
+        sets.append((a, b, torch.empty(cshape, dtype=out_t, device="cuda")))
     return (A, B), sets
 
 
@@ -108,32 +116,52 @@ def traffic_for(kernel, workload):
 def gemm_leg(args, torch):
     name = args.workload
     w = synth.WORKLOADS[name]
-    M, N, K, out = w["M"], w["N"], w["K"], w["out"]
+    M, N, K, out, batch = w["M"], w["N"], w["K"], w["out"], w["batch"]
+    sA, sB, sC = (M * K, N * K, M * N) if batch > 1 else (0, 0, 0)
     log(f"[bench] generating {name} operands")
     (A, B), sets = make_sets(name, torch, args.rotate_mb * 2 ** 20)
     variant = tm.VARIANTS[args.variant]
-    rc, kname, grid, block = tm.gemm_bf16_plan(variant, 1, M, N, K, sets[0][0], K, 0,
-                                               sets[0][1], K, 0, sets[0][2], N, 0, out,
+    rc, kname, grid, block = tm.gemm_bf16_plan(variant, batch, M, N, K, sets[0][0], K, sA,
+                                               sets[0][1], K, sB, sets[0][2], N, sC, out,
                                                torch.cuda.get_device_properties(0).multi_processor_count)
     if rc != 0:
         raise SystemExit(f"variant {args.variant} cannot run {name}: {tm.gemm_bf16_status_string(rc)}")
 
     def launch(i):
         a, b, c = sets[i]
-        tm.gemm_bf16_variant(variant, 1, M, N, K, a, K, 0, b, K, 0, c, N, 0, out)
+        tm.gemm_bf16_variant(variant, batch, M, N, K, a, K, sA, b, K, sB, c, N, sC, out)
 
     log(f"[bench] timing {name}: kernel {kname}, {len(sets)} rotating buffer sets, "
         f"{args.warmup} warm-up + {args.steps} timed steps")
     ms, wall = time_steps(launch, len(sets), args.steps, args.warmup, torch)
-    flops = rl.flops(M, N, K)
+    flops = rl.flops(M, N, K, batch)
     tflops = flops / (ms * 1e-3) / 1e12
     obytes = 4 if out == tm.GEMM_OUT_FP32 else 2
+    nbytes = batch * rl.algorithmic_bytes(M, N, K, obytes)
     return {
-        "name": name, "M": M, "N": N, "K": K, "out": "fp32" if out == 0 else "bf16",
+        "name": name, "batch": batch, "M": M, "N": N, "K": K,
+        "out": "fp32" if out == 0 else "bf16",
         "kernel": kname, "grid": grid, "block": block, "ms": ms, "wall_s": wall,
-        "tflops": tflops, "flops": flops,
-        "bytes": rl.algorithmic_bytes(M, N, K, obytes), "A": A, "B": B, "sets": sets,
+        "tflops": tflops, "flops": flops, "bytes": nbytes, "A": A, "B": B, "sets": sets,
     }
+
+
+def gemm_roofline(res):
+    """The roof that binds this workload (by its arithmetic intensity against the ridge) and
+    the achieved rate against it."""
+    ai = res["flops"] / res["bytes"]
+    bound = rl.bound(rl.MI355X_BF16, ai)
+    if bound == "hbm":
+        gbs = res["bytes"] / (res["ms"] * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": gbs, "peak": HBM_TB_S * 1e3, "unit": "GB/s",
+             "frac": gbs / (HBM_TB_S * 1e3)}
+    else:
+        r = {"bound": "mfma", "achieved": res["tflops"], "peak": MFMA_TFLOPS, "unit": "TFLOP/s",
+             "frac": res["tflops"] / MFMA_TFLOPS}
+    r.update({"traffic": traffic_for(res["kernel"], res["name"]),
+              "flops_per_launch": res["flops"], "algorithmic_bytes_per_launch": res["bytes"],
+              "intensity_flop_per_byte": ai})
+    return r
 
 
 def gemv_leg(args, torch):
@@ -201,6 +229,8 @@ def cpu_baseline_leg(res, args, torch):
     t = time.perf_counter() - t0
     flops = 2.0 * rows * N * K
     out = res["sets"][(args.warmup + args.steps - 1) % len(res["sets"])][2]
+    if res["batch"] > 1:
+        out = out[0]          # the sample is drawn from batch item 0
     got = out[:rows].cpu()
     got = got.numpy() if got.dtype == torch.float32 else got.view(torch.int16).numpy().view(np.uint16)
     od = 0 if res["out"] == "fp32" else 1
@@ -280,17 +310,15 @@ def main():
         "value": res["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["ms"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{res['name']}: C = A B^T, M={res['M']} N={res['N']} "
-                               f"K={res['K']}, bf16 in, fp32 accumulate, {res['out']} out",
+        "config": {"workload": f"{res['name']}: C = A B^T, "
+                               + (f"batch={res['batch']} " if res["batch"] > 1 else "")
+                               + f"M={res['M']} N={res['N']} K={res['K']}, bf16 in, "
+                               f"fp32 accumulate, {res['out']} out",
                    "variant": args.variant, "kernel": res["kernel"],
                    "grid": res["grid"], "block": res["block"],
                    "rotating_buffer_sets": len(res["sets"])},
         "pct_mfma_peak": 100.0 * res["tflops"] / MFMA_TFLOPS,
-        "roofline": {"bound": "mfma", "achieved": res["tflops"], "peak": MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": res["tflops"] / MFMA_TFLOPS,
-                     "traffic": traffic_for(res["kernel"], res["name"]),
-                     "flops_per_launch": res["flops"],
-                     "algorithmic_bytes_per_launch": res["bytes"]},
+        "roofline": gemm_roofline(res),
         "kernel_source_sha": kernel_source_sha(),
     }
     if args.leg == "all" and not args.no_gemv:

@@ -19,9 +19,9 @@
  * tensor's data_ptr() on ROCm) owned by the caller; the library keeps no pointer after a call
  * returns and allocates no memory in any call.  bf16 values are raw 16-bit patterns
  * (uint16_t).  Pitches (lda, ldb, ldc) and batch strides are in ELEMENTS.  A and B must be
- * 2-byte aligned, C 4-byte (fp32 out) or 2-byte (bf16 out) aligned; 16-byte aligned operands
- * with pitches and K multiples of 8 take the fast kernels, anything else a slower general
- * kernel with the same result semantics.  C must not overlap A or B.
+ * 2-byte aligned, C 4-byte (fp32 out) or 2-byte (bf16 out) aligned; 4-byte aligned operands
+ * with even pitches (and strides) take the fast kernels, any K; anything else a slower
+ * general kernel with the same result semantics.  C must not overlap A or B.
  *
  * Streams.  `stream` is a hipStream_t passed as void*; NULL is the default stream.  Calls are
  * asynchronous: they enqueue kernels and return.  A device fault surfaces at the caller's
@@ -97,8 +97,10 @@ int gemm_bf16_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
 /*
  * As gemm_bf16_strided_batched, forcing one GEMM_VARIANT_* kernel (for ablations and the
  * measurements of each rung).  A variant whose preconditions the arguments do not meet
- * (GEMV with M > 16; the pipelined and persistent variants need 16-byte aligned A and B,
- * lda, ldb, strides and K multiples of 8) returns GEMM_ERR_UNSUPPORTED and does nothing.
+ * (GEMV with M > 16, or with A, B not 16-byte aligned or lda, ldb, K not multiples of 8;
+ * the pipelined, persistent and specialized variants need 4-byte aligned A and B and even
+ * lda, ldb and strides; the ping-pong variant 16-byte aligned A and B and lda, ldb, strides
+ * and K multiples of 8) returns GEMM_ERR_UNSUPPORTED and does nothing.
  * An unknown variant returns GEMM_ERR_ARG.
  */
 int gemm_bf16_variant(int variant, int64_t batch, int64_t M, int64_t N, int64_t K,

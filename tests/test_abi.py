@@ -78,8 +78,10 @@ def test_plan_workloads():
     assert plan(M=8192, N=14336, K=4096, out=1)[:2] == (0, "spec_256")
     assert plan(variant=5)[:2] == (0, "spec_256")
     assert plan(variant=5)[3] == 512
-    # K = 4100 with lda = 4100: rows are only 8-byte aligned -> general MFMA kernel
-    assert plan(M=3000, N=5000, K=4100)[1] == "mfma_128"
+    # K = 4100 with lda = 4100: rows 8-byte aligned, ragged K tail -> still the eight-wave kernel
+    assert plan(M=3000, N=5000, K=4100)[1] == "spec_256"
+    # odd pitch: rows only 2-byte aligned -> general MFMA kernel
+    assert plan(M=3000, N=5000, K=4101)[1] == "mfma_128"
     assert plan(batch=64, M=256, N=256, K=1024, sA=256 * 1024, sB=256 * 1024,
                 sC=256 * 256)[1] == "persist_128"
     assert plan(K=0, lda=1, ldb=1)[:2] == (0, "zero_fill")
@@ -95,11 +97,21 @@ def test_plan_persistent_grid_is_cu_count():
 
 def test_plan_variant_preconditions():
     assert plan(variant=6, M=17)[0] == tm.GEMM_ERR_UNSUPPORTED
-    assert plan(variant=3, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
+    # pipelined / persistent / specialized: 4-byte aligned rows, any K
+    assert plan(variant=3, K=4100)[:2] == (0, "pipe_256")
+    assert plan(variant=3, K=4099, lda=4100, ldb=4100)[:2] == (0, "pipe_256")
+    assert plan(variant=3, K=4099)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=4, A=P + 4)[:2] == (0, "persist_256")
     assert plan(variant=4, A=P + 2)[0] == tm.GEMM_ERR_UNSUPPORTED
-    assert plan(variant=8)[0] == tm.GEMM_ERR_ARG
+    assert plan(variant=5, K=4100)[:2] == (0, "spec_256")
+    assert plan(variant=5, K=7, lda=8, ldb=10)[:2] == (0, "spec_256")
+    assert plan(variant=5, batch=2, sA=4096 * 4096 + 1, sB=4096 * 4096,
+                sC=4096 * 4096)[0] == tm.GEMM_ERR_UNSUPPORTED
+    # ping-pong: 16-byte aligned rows and K % 8 == 0
     assert plan(variant=7)[:2] == (0, "pingpong_256")
-    assert plan(variant=5, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=7, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=7, A=P + 8)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=8)[0] == tm.GEMM_ERR_ARG
     assert plan(variant=1)[1] == "simple_64"
     assert plan(variant=2)[1] == "mfma_128"
 

@@ -126,9 +126,31 @@ def test_padded_pitches(variant):
     assert_exact(got, A, B, K, OUT_FP32, what="padded pitches")
 
 
+# Ragged K (not a multiple of 8) and rows that are only 4- or 8-byte aligned: the pipelined
+# kernels load whole 16-byte chunks below K rounded down to 8 and add the rest in one extra
+# k step.  Pitch padding holds NaN, so a tail element read from beyond K would show.
+RAGGED = [(130, 260, 77), (260, 129, 1027), (64, 64, 7), (300, 520, 100), (257, 300, 2053),
+          (513, 257, 4)]
+PIPE_VARIANTS = [V.GEMM_VARIANT_PIPELINED, V.GEMM_VARIANT_PERSISTENT,
+                 V.GEMM_VARIANT_SPECIALIZED, V.GEMM_VARIANT_AUTO]
+
+
+@pytest.mark.parametrize("variant", PIPE_VARIANTS)
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_ragged_k_and_4byte_rows(variant, M, N, K):
+    lda = K + (K % 2)          # even: rows start on 4-byte boundaries
+    ldb = K + 2 - (K % 2)
+    A = synth.integers(M, K, 301 + K, ld=lda)
+    B = synth.integers(N, K, 302 + K, ld=ldb)
+    for out_dtype in (OUT_FP32, OUT_BF16):
+        got = run_gemm(A, B, K, out_dtype, variant=variant, a_offset=2, b_offset=6)
+        assert_exact(got, A, B, K, out_dtype, what=f"variant {variant} {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("lda_pad", [1, 3, 4])
 def test_unaligned_pitches_and_k(lda_pad):
-    """Pitches and K that are not multiples of 8 go to the general kernel."""
+    """Pitches and K that are not multiples of 8 (odd ldb with lda_pad 4: the general
+    kernel; even pitches: the pipelined kernels with a ragged K tail)."""
     M, N, K = 130, 140, 100 + lda_pad
     A = synth.integers(M, K, 41, ld=K + lda_pad)
     B = synth.integers(N, K, 42, ld=K + 1)

@@ -77,11 +77,22 @@ struct Shape {
     int out;
 };
 
-// The direct-to-LDS kernels: 16-byte chunks that never straddle K, 32-bit buffer offsets.
+// The ping-pong kernel: 16-byte aligned rows, 16-byte chunks that never straddle K, 32-bit
+// buffer offsets.
 bool fast_loads_ok(const Shape& s, int rows) {
     if (!aligned(s.A, 16) || !aligned(s.B, 16)) return false;
     if (s.lda % 8 || s.ldb % 8 || s.K % 8) return false;
     if (s.batch > 1 && (s.sA % 8 || s.sB % 8)) return false;
+    return int64_t(rows) * s.lda * 2 < k2G && int64_t(rows) * s.ldb * 2 < k2G;
+}
+
+// The pipelined kernels: the same 16-byte direct-to-LDS loads from rows that start on a
+// 4-byte boundary (gfx950 serves unaligned buffer loads), with a ragged K tail added by
+// one extra k step.
+bool pipe_loads_ok(const Shape& s, int rows) {
+    if (!aligned(s.A, 4) || !aligned(s.B, 4)) return false;
+    if (s.lda % 2 || s.ldb % 2) return false;
+    if (s.batch > 1 && (s.sA % 2 || s.sB % 2)) return false;
     return int64_t(rows) * s.lda * 2 < k2G && int64_t(rows) * s.ldb * 2 < k2G;
 }
 
@@ -129,7 +140,7 @@ bool use_big_tile(const Shape& s, int cus) {
 
 int plan_pipe(const Shape& s, bool persistent, int cus, Plan& p) {
     const bool big = use_big_tile(s, cus);
-    if (!fast_loads_ok(s, big ? 256 : 128)) return GEMM_ERR_UNSUPPORTED;
+    if (!pipe_loads_ok(s, big ? 256 : 128)) return GEMM_ERR_UNSUPPORTED;
     tile_grid(s, big ? 256 : 128, big ? 256 : 128, p);
     p.kernel = persistent ? (big ? K_PERSIST_256 : K_PERSIST_128) : (big ? K_PIPE_256 : K_PIPE_128);
     p.grid_x = persistent ? std::min(p.grid.total, cus) : p.grid.total;
@@ -143,7 +154,7 @@ int plan_pipe(const Shape& s, bool persistent, int cus, Plan& p) {
 // `kernel`: K_SPEC_256 (both groups load and multiply in lockstep) or K_PINGPONG_256 (the
 // groups alternate load and MFMA phases).
 int plan_spec(const Shape& s, int cus, Plan& p, int kernel = K_SPEC_256) {
-    if (!fast_loads_ok(s, 256)) return GEMM_ERR_UNSUPPORTED;
+    if (kernel == K_PINGPONG_256 ? !fast_loads_ok(s, 256) : !pipe_loads_ok(s, 256)) return GEMM_ERR_UNSUPPORTED;
     tile_grid(s, 256, 256, p);
     p.kernel = kernel;
     p.grid_x = std::min(p.grid.total, cus);

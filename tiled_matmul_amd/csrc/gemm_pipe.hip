@@ -24,9 +24,11 @@
 //     w, w + grid, ... through tile_of(), the XCD-aware grouped order.  While a finished
 //     tile is written back, the next tile's first stages are already loading.
 //
-// Preconditions checked by the planner: K % 8 == 0, lda, ldb, strideA, strideB multiples
-// of 8 and A, B 16-byte aligned, BM * lda * 2 and BN * ldb * 2 below 2^31.  Rows beyond M
-// (N) and k-chunks beyond K are turned into out-of-range buffer offsets, which read zeros.
+// Preconditions checked by the planner: A, B 4-byte aligned, lda, ldb, strideA, strideB
+// even (every row starts on a 4-byte boundary; the 16-byte loads do not need more),
+// BM * lda * 2 and BN * ldb * 2 below 2^31.  Rows beyond M (N) and k-chunks beyond K8 = K
+// rounded down to a multiple of 8 are turned into out-of-range buffer offsets, which read
+// zeros; the remaining K - K8 < 8 columns enter through one extra k step after the loop.
 #include "launch.hpp"
 
 namespace tmm {
@@ -142,10 +144,6 @@ struct Frags {
     bf16x8 a[FM];
 };
 
-#ifndef TMM_PREFETCH
-#define TMM_PREFETCH 0
-#endif
-
 template <int BM, int BN, int BK, int STAGES, int SWZ, int MF, int OUT, bool XCD_ORDER, int WAVES_M,
           int WAVES_N>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void gemm_pipe_kernel(
@@ -155,22 +153,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     constexpr int KSTEPS = BK / T::KS;
     constexpr bool FINE = WAVES_M * WAVES_N >= 8;   // see step()
     constexpr int FN = P::WN / T::ROWS, FM = P::WM / T::ROWS;   // fragments per wave
-    // L2 prefetch: with PF > 0, each block's loads are followed by a touch of every
-    // 128-byte row segment of block kb + PF, so that block's own loads find their lines in L2
-    // (the first touch of a cold operand otherwise puts HBM latency inside a ring only
-    // STAGES - 1 blocks deep).  One dword per line, PFN instructions per wave per block,
-    // landing in a 256-byte LDS sink per wave that nothing reads.
-    constexpr int PF = TMM_PREFETCH;
-    constexpr int PFN = PF > 0 ? (BM + BN + 64 * P::NW - 1) / (64 * P::NW) : 0;
     // Loads issued after the last load of block kb + 1 when block kb + 1 must have landed.
-    constexpr int WAIT_N = (STAGES - 2) * P::LOADS + (STAGES - 1) * PFN;
-    static_assert(WAIT_N <= 63, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * P::STAGE_BYTES + (PF > 0 ? 256 * P::NW : 0)];
+    constexpr int WAIT_N = (STAGES - 2) * P::LOADS;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * P::STAGE_BYTES];
 
     const int lane = lane_id(), w = wave_id();
     const int wm = w / WAVES_N, wn = w % WAVES_N;
     const int nk = static_cast<int>((g.K + BK - 1) / BK);
     const uint32_t K = static_cast<uint32_t>(g.K);
+    // The 16-byte loads cover k < K8; a ragged tail K8 <= k < K (K not a multiple of 8) is
+    // added by one more MFMA step after the loop.
+    const uint32_t K8 = K & ~7u;
     constexpr int NW = P::NW;
 
     // Per-lane element k offset of the 16-byte chunk this lane moves in each of its load
@@ -235,10 +228,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
             const uint32_t soff = 2u * k0;
 #pragma unroll
             for (int i = 0; i < P::IA; ++i)
-                load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2, k0 + chunk_k[i] < K ? va[i] : OOB, soff);
+                load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2, k0 + chunk_k[i] < K8 ? va[i] : OOB, soff);
 #pragma unroll
             for (int i = 0; i < P::IB; ++i)
-                load_lds_16(rb, sb + (NW * i + w) * P::R * BK * 2, k0 + chunk_k[i] < K ? vb[i] : OOB, soff);
+                load_lds_16(rb, sb + (NW * i + w) * P::R * BK * 2, k0 + chunk_k[i] < K8 ? vb[i] : OOB, soff);
         };
         auto read_frags = [&](Frags<FN, FM>& f, int slot, int kk) {
             const uint8_t* base = lds + slot * P::STAGE_BYTES + rd[kk];
@@ -255,28 +248,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
             uint8_t* sa = lds + slot * P::STAGE_BYTES;
             const uint32_t k0 = static_cast<uint32_t>(kb) * BK;
             if (i < P::IA)
-                load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2, k0 + chunk_k[i] < K ? va[i] : OOB, 2u * k0);
+                load_lds_16(ra, sa + (NW * i + w) * P::R * BK * 2, k0 + chunk_k[i] < K8 ? va[i] : OOB, 2u * k0);
             else
                 load_lds_16(rb, sa + P::A_BYTES + (NW * (i - P::IA) + w) * P::R * BK * 2,
-                            k0 + chunk_k[i - P::IA] < K ? vb[i - P::IA] : OOB, 2u * k0);
-        };
-        // L2 prefetch of block kb: lane l of wave w, instruction p covers tile row
-        // (p NW + w) 64 + l (A rows first, then B rows).
-        auto prefetch = [&](int kb) {
-            if constexpr (PF > 0) {
-                const uint32_t k0 = static_cast<uint32_t>(kb) * BK;
-#pragma unroll
-                for (int p = 0; p < PFN; ++p) {
-                    const int r = (p * P::NW + w) * 64 + lane;
-                    uint32_t off = OOB;
-                    if (k0 < K) {
-                        if (r < BM) off = r < rows_a ? static_cast<uint32_t>(r * g.lda) * 2u : OOB;
-                        else if (r < BM + BN) off = r - BM < rows_b ? static_cast<uint32_t>((r - BM) * g.ldb) * 2u : OOB;
-                    }
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r < BM ? ra : rb, (lds_ptr_t)(lds + STAGES * P::STAGE_BYTES + 256 * w),
-                                                             4, off, 2u * k0, 0, 0);
-                }
-            }
+                            k0 + chunk_k[i - P::IA] < K8 ? vb[i - P::IA] : OOB, 2u * k0);
         };
         // One fragment (q < FN: B fragment q, else A fragment q - FN) of k step kk of `slot`.
         auto read_one = [&](Frags<FN, FM>& f, int q, int slot, int kk) {
@@ -297,14 +272,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         // fragments of block 0's first k step.  (Every wave has passed the previous tile's
         // final barrier, so the whole ring is free.)
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s) {
-            issue(s, s);
-            prefetch(s + PF);
-        }
+        for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
         wait_vmcnt<WAIT_N>();
         barrier();
         issue(STAGES - 1, STAGES - 1);
-        prefetch(STAGES - 1 + PF);
         Frags<FN, FM> f[2];
         read_frags(f[0], 0, 0);
         wait_cnt<63, 0>();
@@ -329,7 +300,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
             barrier();
             step<FN, FM, FN + FM, P::LOADS, FINE>(acc, f[LAST], [&](int q) { read_one(f[LAST ^ 1], q, next_slot, 0); },
                                             [&](int q) { issue_one(q, kb + STAGES, slot); });
-            prefetch(kb + STAGES + PF);
             // The reads of block kb+1's first fragments were interleaved with the MFMAs just
             // issued and have long completed; saying so here keeps the compiler from stalling
             // the next iteration's first MFMA on a conservative lgkmcnt.
@@ -345,6 +315,41 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         }
         wait_vmcnt<0>();   // the trailing zero-fill loads have landed
         barrier();  // all fragment reads of this tile are done before the ring is refilled
+
+        if (K8 != K) {
+            // Ragged K tail: one more k step over k = K8 .. K8 + KS - 1 whose first 16-byte
+            // chunk holds elements K8 .. K - 1 of each row and everything else is zero.
+            // Each thread stages whole rows into ring slot 0 (free since the barrier above),
+            // element by element so nothing at or beyond K is read; then every wave reads
+            // its fragments as in the loop.
+            const uint16_t* Ag = g.A + bt * g.sA + m0 * g.lda;
+            const uint16_t* Bg = g.B + bt * g.sB + n0 * g.ldb;
+            for (int r = threadIdx.x; r < BM + BN; r += 64 * NW) {
+                const bool is_a = r < BM;
+                const int rr = is_a ? r : r - BM;
+                uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (rr < (is_a ? rows_a : rows_b)) {
+                    const uint16_t* row = is_a ? Ag + rr * g.lda : Bg + rr * g.ldb;
+#pragma unroll
+                    for (int e = 0; e < 7; ++e)
+                        if (K8 + e < K) h[e] = row[K8 + e];
+                }
+                uint8_t* dst = lds + (is_a ? 0 : P::A_BYTES) + rr * BK * 2;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                const u32x4 v = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+#pragma unroll
+                for (int c = 0; c < T::KS / 8; ++c)
+                    *reinterpret_cast<u32x4*>(dst + ((c ^ P::swz(rr)) * 16)) = c == 0 ? v : z;
+            }
+            barrier();
+            read_frags(f[0], 0, 0);
+            wait_cnt<63, 0>();
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) acc[i][j] = T::run(f[0].b[i], f[0].a[j], acc[i][j]);
+            barrier();   // the ring is read before the next tile refills it
+        }
 
         void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
                                   : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
