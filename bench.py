@@ -164,11 +164,10 @@ def gemm_roofline(res):
     return r
 
 
-def gemv_leg(args, torch):
-    name = "gemv_m1"
+def gemv_leg(args, torch, name="gemv_m1"):
     w = synth.WORKLOADS[name]
     M, N, K, out = w["M"], w["N"], w["K"], w["out"]
-    log("[bench] generating gemv_m1 operands")
+    log(f"[bench] generating {name} operands")
     (A, B), sets = make_sets(name, torch, 2 * MALL_BYTES + 32 * 2 ** 20)
     n = len(sets)
 
@@ -196,12 +195,14 @@ def gemv_leg(args, torch):
     torch.cuda.synchronize()
     launches = reps * n * args.gemv_replays
     us = start.elapsed_time(end) * 1e3 / launches
-    nbytes = rl.algorithmic_bytes(M, N, K, 4)
+    nbytes = rl.algorithmic_bytes(M, N, K, 4 if out == tm.GEMM_OUT_FP32 else 2)
     gbs = nbytes / (us * 1e-6) / 1e9
     _, kname, grid, block = tm.gemm_bf16_plan(0, 1, M, N, K, sets[0][0], K, 0, sets[0][1], K, 0,
                                               sets[0][2], N, 0, out)
     return {
-        "metric": "GB/s and % of HBM peak, decode GEMV M=1 N=K=4096 (bf16 in, fp32 out)",
+        "metric": f"GB/s and % of HBM peak, decode GEMV M={M} N={N} K={K} (bf16 in, "
+                  f"{'fp32' if out == tm.GEMM_OUT_FP32 else 'bf16'} out)",
+        "workload": name,
         "value": gbs, "unit": "GB/s", "us_per_launch": us, "launches": launches,
         "kernel": kname, "grid": grid, "block": block, "rotating_weight_buffers": n,
         "timing": "HIP events around replays of a captured HIP graph of back-to-back launches",
@@ -275,6 +276,8 @@ def main():
     ap.add_argument("--variant", default="auto", choices=sorted(tm.VARIANTS))
     ap.add_argument("--rotate-mb", type=int, default=512,
                     help="total size of the rotating input/output sets")
+    ap.add_argument("--gemv-workload", default="gemv_m1", choices=["gemv_m1", "gemv_m16"],
+                    help="workload of the GEMV leg")
     ap.add_argument("--gemv-launches", type=int, default=340)
     ap.add_argument("--gemv-replays", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -301,7 +304,8 @@ def main():
         copy_leg(args, torch)
         return
     if args.leg == "gemv":
-        print(json.dumps({"gemv": gemv_leg(args, torch), "kernel_source_sha": kernel_source_sha()}))
+        print(json.dumps({"gemv": gemv_leg(args, torch, args.gemv_workload),
+                          "kernel_source_sha": kernel_source_sha()}))
         return
 
     res = gemm_leg(args, torch)

@@ -70,8 +70,10 @@ def plan(variant=0, batch=1, M=4096, N=4096, K=4096, A=P, lda=None, sA=0, B=P, l
 
 def test_plan_workloads():
     assert plan()[:2] == (0, "spec_256")
-    assert plan(M=1)[:2] == (0, "gemv_dot")
-    assert plan(M=8)[:2] == (0, "gemv_dot")
+    assert plan(M=1)[:2] == (0, "gemv_lds")
+    assert plan(M=4)[:2] == (0, "gemv_lds")
+    assert plan(M=5)[:2] == (0, "gemv")
+    assert plan(M=8)[:2] == (0, "gemv")
     assert plan(M=9)[:2] == (0, "gemv")
     assert plan(M=16)[:2] == (0, "gemv")
     assert plan(M=17)[1] != "gemv"

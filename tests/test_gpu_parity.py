@@ -85,8 +85,9 @@ def test_integer_exact_variants(variant, out_dtype, M, N, K):
 
 
 @pytest.mark.parametrize("variant", [V.GEMM_VARIANT_GEMV, V.GEMM_VARIANT_AUTO])
-@pytest.mark.parametrize("M", [1, 2, 7, 16])
-@pytest.mark.parametrize("N,K", [(4096, 4096), (100, 264), (17, 8), (300, 1000)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 9, 16])
+@pytest.mark.parametrize("N,K", [(4096, 4096), (100, 264), (17, 8), (300, 1000), (33, 4360),
+                                 (70, 8200)])
 def test_integer_exact_gemv(variant, M, N, K):
     A = synth.integers(M, K, 21 + M)
     B = synth.integers(N, K, 22 + N)

@@ -110,6 +110,21 @@ __device__ __forceinline__ void barrier() {
     asm volatile("" ::: "memory");
 }
 
+// s_waitcnt through the builtin, so that the compiler's own wait insertion sees it.  gfx9
+// encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]; an all-ones field
+// does not wait on that counter.
+template <int VM, int LGKM = 15>
+__device__ __forceinline__ void wait_cnt() {
+    static_assert(VM >= 0 && VM <= 63 && LGKM >= 0 && LGKM <= 15, "counter range");
+    constexpr int enc = (VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14);
+    __builtin_amdgcn_s_waitcnt(enc);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    wait_cnt<N, 15>();
+}
+
 }  // namespace tmm
 
 namespace tmm {

@@ -170,13 +170,19 @@ bool gemv_ok(const Shape& s) {
     return 16 * s.lda * 2 < k2G && 16 * s.ldb * 2 < k2G && cdiv(s.N, 16) < k2G;
 }
 
-// M <= 8: the dot-product form; 8 < M <= 16: the MFMA form.
+// Largest M that takes the dot-product form of the skinny-M path (above it, up to 16: the
+// MFMA form).  Measured on MI355X at N = K = 4096: the dot form is faster up to M = 4
+// (6.8 us at M = 1), the MFMA form from M = 8 (9.9 us at M = 8 and at M = 16).
+#ifndef TMM_GEMV_DOT_MAX_M
+#define TMM_GEMV_DOT_MAX_M 4
+#endif
+
 int plan_gemv(const Shape& s, Plan& p) {
     if (!gemv_ok(s)) return GEMM_ERR_UNSUPPORTED;
-    if (s.M <= 8) {
-        p.kernel = K_GEMV_DOT;
-        p.grid_x = static_cast<int>(cdiv(s.N, gemv_dot_rows_per_workgroup()));
-        p.block = 256;
+    if (s.M <= TMM_GEMV_DOT_MAX_M) {
+        p.kernel = K_GEMV_LDS;
+        p.grid_x = static_cast<int>(cdiv(s.N, gemv_lds_rows_per_workgroup()));
+        p.block = gemv_lds_threads();
     } else {
         p.kernel = K_GEMV;
         p.grid_x = static_cast<int>(cdiv(s.N, 16));
@@ -248,7 +254,7 @@ int run(int variant, const Shape& s, void* stream) {
         case K_SPEC_256: e = launch_pipe(g, s.out, p, st); break;
         case K_PINGPONG_256: e = launch_pingpong(g, s.out, p, st); break;
         case K_GEMV: e = launch_gemv(g, s.out, p, st); break;
-        case K_GEMV_DOT: e = launch_gemv_dot(g, s.out, p, st); break;
+        case K_GEMV_LDS: e = launch_gemv_lds(g, s.out, p, st); break;
         default: return GEMM_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
@@ -318,7 +324,7 @@ const char* gemm_bf16_kernel_name(int k) {
         case K_SPEC_256: return "spec_256";
         case K_PINGPONG_256: return "pingpong_256";
         case K_GEMV: return "gemv";
-        case K_GEMV_DOT: return "gemv_dot";
+        case K_GEMV_LDS: return "gemv_lds";
         default: return "?";
     }
 }

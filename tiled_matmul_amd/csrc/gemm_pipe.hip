@@ -56,21 +56,6 @@ struct PipeCfg {
     }
 };
 
-// s_waitcnt through the builtin, so that the compiler's own wait insertion sees it.  gfx9
-// encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]; an all-ones field
-// does not wait on that counter.
-template <int VM, int LGKM = 15>
-__device__ __forceinline__ void wait_cnt() {
-    static_assert(VM >= 0 && VM <= 63 && LGKM >= 0 && LGKM <= 15, "counter range");
-    constexpr int enc = (VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14);
-    __builtin_amdgcn_s_waitcnt(enc);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    wait_cnt<N, 15>();
-}
-
 // The two bf16 MFMA shapes of gfx950.  ROWS x ROWS output block per instruction, KS = k
 // depth per instruction; lane l supplies row (l % ROWS) and the 8-element k chunk
 // (l / ROWS) of each operand.
@@ -144,8 +129,10 @@ struct Frags {
     bf16x8 a[FM];
 };
 
+// RAGGED: K is not a multiple of 8 (a separate instance, so that the common case carries
+// none of the tail code and none of the registers it holds).
 template <int BM, int BN, int BK, int STAGES, int SWZ, int MF, int OUT, bool XCD_ORDER, int WAVES_M,
-          int WAVES_N>
+          int WAVES_N, bool RAGGED>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void gemm_pipe_kernel(
     GemmArgs g, TileGrid tg, int vec_store) {
     typedef PipeCfg<BM, BN, BK, STAGES, SWZ, WAVES_M, WAVES_N> P;
@@ -163,7 +150,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     const uint32_t K = static_cast<uint32_t>(g.K);
     // The 16-byte loads cover k < K8; a ragged tail K8 <= k < K (K not a multiple of 8) is
     // added by one more MFMA step after the loop.
-    const uint32_t K8 = K & ~7u;
+    const uint32_t K8 = RAGGED ? K & ~7u : K;
     constexpr int NW = P::NW;
 
     // Per-lane element k offset of the 16-byte chunk this lane moves in each of its load
@@ -316,7 +303,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         wait_vmcnt<0>();   // the trailing zero-fill loads have landed
         barrier();  // all fragment reads of this tile are done before the ring is refilled
 
-        if (K8 != K) {
+        if constexpr (RAGGED) {
             // Ragged K tail: one more k step over k = K8 .. K8 + KS - 1 whose first 16-byte
             // chunk holds elements K8 .. K - 1 of each row and everything else is zero.
             // Each thread stages whole rows into ring slot 0 (free since the barrier above),
@@ -375,12 +362,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
 template <int BM, int BN, int BK, int STAGES, int SWZ, bool XCD, int MF = TMM_MFMA, int WM = 2, int WN = 2>
 static hipError_t launch_pipe_cfg(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
     constexpr int THREADS = 64 * WM * WN;
-    if (out == OUT_F32)
-        hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, BK, STAGES, SWZ, MF, OUT_F32, XCD, WM, WN>),
-                           dim3(p.grid_x), dim3(THREADS), 0, s, g, p.grid, p.vec_store);
-    else
-        hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, BK, STAGES, SWZ, MF, OUT_BF16, XCD, WM, WN>),
-                           dim3(p.grid_x), dim3(THREADS), 0, s, g, p.grid, p.vec_store);
+    const bool ragged = (g.K & 7) != 0;
+#define TMM_LAUNCH(O, R)                                                                          \
+    hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, BK, STAGES, SWZ, MF, O, XCD, WM, WN, R>), dim3(p.grid_x), \
+                       dim3(THREADS), 0, s, g, p.grid, p.vec_store)
+    if (out == OUT_F32 && ragged) {
+        TMM_LAUNCH(OUT_F32, true);
+    } else if (out == OUT_F32) {
+        TMM_LAUNCH(OUT_F32, false);
+    } else if (ragged) {
+        TMM_LAUNCH(OUT_BF16, true);
+    } else {
+        TMM_LAUNCH(OUT_BF16, false);
+    }
+#undef TMM_LAUNCH
     return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ enum KernelId {
     K_PERSIST_128 = 7,      //   same, 128x128
     K_SPEC_256 = 8,         // ladder step 5: wave-specialised, two consumer groups share B
     K_GEMV = 9,             // ladder step 6: skinny-M bandwidth path, MFMA form (M <= 16)
-    K_GEMV_DOT = 10,        //   same, dot-product form with contiguous loads (M <= 8)
+    K_GEMV_LDS = 10,        //   same, dot-product form: contiguous W rows, X staged in LDS
     K_PINGPONG_256 = 11,    // ladder steps 7-9: two wave groups alternate load and MFMA phases
     K_COUNT = 12
 };
@@ -40,7 +40,8 @@ hipError_t launch_mfma(const GemmArgs& g, int out, const Plan& p, hipStream_t s)
 hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_pingpong(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
-hipError_t launch_gemv_dot(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
-int gemv_dot_rows_per_workgroup();
+hipError_t launch_gemv_lds(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+int gemv_lds_rows_per_workgroup();
+int gemv_lds_threads();
 
 }  // namespace tmm
