@@ -63,6 +63,8 @@ extern "C" {
 #define GEMM_VARIANT_SPECIALIZED 5 /* steps 7-9: producer/consumer waves sharing the B tile    */
 #define GEMM_VARIANT_GEMV 6        /* skinny M (M <= 16): bandwidth-bound decode path         */
 #define GEMM_VARIANT_PINGPONG 7    /* steps 7-9: two wave groups alternate load / MFMA phases  */
+#define GEMM_VARIANT_RING8 8       /* steps 4-6, 5-slot ring of 32-deep K sub-blocks, 8 waves  */
+#define GEMM_VARIANT_RING4 9       /* the same with 4 waves of 128x128 register tiles          */
 
 /*
  * C = A * B^T for one problem (definition above).

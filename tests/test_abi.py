@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tm.gemm_bf16_version() == 2
+    assert tm.gemm_bf16_version() == 3
     for s in range(7):
         assert tm.gemm_bf16_status_string(s).startswith("GEMM_")
     assert tm.gemm_bf16_status_string(99) == "unknown status"
@@ -69,7 +69,8 @@ def plan(variant=0, batch=1, M=4096, N=4096, K=4096, A=P, lda=None, sA=0, B=P, l
 
 
 def test_plan_workloads():
-    assert plan()[:2] == (0, "spec_256")
+    assert plan()[:2] == (0, "ring4_256")
+    assert plan()[3] == 256
     assert plan(M=1)[:2] == (0, "gemv_lds")
     assert plan(M=4)[:2] == (0, "gemv_lds")
     assert plan(M=5)[:2] == (0, "gemv")
@@ -77,11 +78,11 @@ def test_plan_workloads():
     assert plan(M=9)[:2] == (0, "gemv")
     assert plan(M=16)[:2] == (0, "gemv")
     assert plan(M=17)[1] != "gemv"
-    assert plan(M=8192, N=14336, K=4096, out=1)[:2] == (0, "spec_256")
+    assert plan(M=8192, N=14336, K=4096, out=1)[:2] == (0, "ring4_256")
     assert plan(variant=5)[:2] == (0, "spec_256")
     assert plan(variant=5)[3] == 512
-    # K = 4100 with lda = 4100: rows 8-byte aligned, ragged K tail -> still the eight-wave kernel
-    assert plan(M=3000, N=5000, K=4100)[1] == "spec_256"
+    # K = 4100 with lda = 4100: rows 8-byte aligned, ragged K tail -> still the fast kernel
+    assert plan(M=3000, N=5000, K=4100)[1] == "ring4_256"
     # odd pitch: rows only 2-byte aligned -> general MFMA kernel
     assert plan(M=3000, N=5000, K=4101)[1] == "mfma_128"
     assert plan(batch=64, M=256, N=256, K=1024, sA=256 * 1024, sB=256 * 1024,
@@ -113,7 +114,14 @@ def test_plan_variant_preconditions():
     assert plan(variant=7)[:2] == (0, "pingpong_256")
     assert plan(variant=7, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
     assert plan(variant=7, A=P + 8)[0] == tm.GEMM_ERR_UNSUPPORTED
-    assert plan(variant=8)[0] == tm.GEMM_ERR_ARG
+    # five-slot ring, 8 and 4 waves: the pipelined kernels' preconditions
+    assert plan(variant=8)[:2] == (0, "ring8_256")
+    assert plan(variant=8)[3] == 512
+    assert plan(variant=9)[:2] == (0, "ring4_256")
+    assert plan(variant=9)[3] == 256
+    assert plan(variant=9, K=4099, lda=4100, ldb=4100)[:2] == (0, "ring4_256")
+    assert plan(variant=9, A=P + 2)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=10)[0] == tm.GEMM_ERR_ARG
     assert plan(variant=1)[1] == "simple_64"
     assert plan(variant=2)[1] == "mfma_128"
 

@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 V = tm
 ALL_TILED = [V.GEMM_VARIANT_SIMPLE, V.GEMM_VARIANT_MFMA, V.GEMM_VARIANT_PIPELINED,
              V.GEMM_VARIANT_PERSISTENT, V.GEMM_VARIANT_SPECIALIZED, V.GEMM_VARIANT_PINGPONG,
-             V.GEMM_VARIANT_AUTO]
+             V.GEMM_VARIANT_RING8, V.GEMM_VARIANT_RING4, V.GEMM_VARIANT_AUTO]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -133,7 +133,8 @@ def test_padded_pitches(variant):
 RAGGED = [(130, 260, 77), (260, 129, 1027), (64, 64, 7), (300, 520, 100), (257, 300, 2053),
           (513, 257, 4)]
 PIPE_VARIANTS = [V.GEMM_VARIANT_PIPELINED, V.GEMM_VARIANT_PERSISTENT,
-                 V.GEMM_VARIANT_SPECIALIZED, V.GEMM_VARIANT_AUTO]
+                 V.GEMM_VARIANT_SPECIALIZED, V.GEMM_VARIANT_RING8, V.GEMM_VARIANT_RING4,
+                 V.GEMM_VARIANT_AUTO]
 
 
 @pytest.mark.parametrize("variant", PIPE_VARIANTS)

@@ -25,7 +25,8 @@ CFLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
 # Per-file compiler options.  The pipelined GEMM keeps MFMA fragments live across its K-block
 # loop; LLVM's default scheduler then over-commits VGPRs and shuffles accumulators through
 # AGPR copies, which the iterative ILP scheduler avoids.
-FILE_FLAGS = {"gemm_pipe.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+FILE_FLAGS = {"gemm_pipe.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+              "gemm_ring.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:

@@ -11,7 +11,7 @@ using namespace tmm;
 
 namespace {
 
-constexpr int kVersion = 2;
+constexpr int kVersion = 3;
 constexpr int kDefaultCUs = 256;        // MI355X
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t k2G = int64_t(1) << 31;
@@ -159,7 +159,7 @@ int plan_spec(const Shape& s, int cus, Plan& p, int kernel = K_SPEC_256) {
     p.kernel = kernel;
     p.grid_x = std::min(p.grid.total, cus);
     p.grid_y = p.grid_z = 1;
-    p.block = 512;
+    p.block = kernel == K_RING4_256 ? 256 : 512;
     p.vec_store = vec_store_ok(s);
     return GEMM_OK;
 }
@@ -193,7 +193,7 @@ int plan_gemv(const Shape& s, Plan& p) {
 }
 
 int make_plan(int variant, const Shape& s, int cus, Plan& p) {
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_PINGPONG) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_RING4) return GEMM_ERR_ARG;
     p = Plan{};
     if (s.batch == 0 || s.M == 0 || s.N == 0) {
         p.kernel = K_NONE;
@@ -214,11 +214,13 @@ int make_plan(int variant, const Shape& s, int cus, Plan& p) {
         case GEMM_VARIANT_SPECIALIZED: return plan_spec(s, cus, p);
         case GEMM_VARIANT_GEMV: return plan_gemv(s, p);
         case GEMM_VARIANT_PINGPONG: return plan_spec(s, cus, p, K_PINGPONG_256);
+        case GEMM_VARIANT_RING8: return plan_spec(s, cus, p, K_RING8_256);
+        case GEMM_VARIANT_RING4: return plan_spec(s, cus, p, K_RING4_256);
         default: break;
     }
     // AUTO
     if (gemv_ok(s)) return plan_gemv(s, p);
-    if (use_big_tile(s, cus) && plan_spec(s, cus, p) == GEMM_OK) return GEMM_OK;
+    if (use_big_tile(s, cus) && plan_spec(s, cus, p, K_RING4_256) == GEMM_OK) return GEMM_OK;
     if (plan_pipe(s, true, cus, p) == GEMM_OK) return GEMM_OK;
     int rc = plan_2d(s, K_MFMA_128, 128, p);
     if (rc == GEMM_OK) return rc;
@@ -228,7 +230,7 @@ int make_plan(int variant, const Shape& s, int cus, Plan& p) {
 int run(int variant, const Shape& s, void* stream) {
     int rc = validate(s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC, s.out);
     if (rc != GEMM_OK) return rc;
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_PINGPONG) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_RING4) return GEMM_ERR_ARG;
     if (s.batch == 0 || s.M == 0 || s.N == 0) return GEMM_OK;
     int cus = 0;
     rc = current_device(&cus);
@@ -253,6 +255,8 @@ int run(int variant, const Shape& s, void* stream) {
         case K_PERSIST_128:
         case K_SPEC_256: e = launch_pipe(g, s.out, p, st); break;
         case K_PINGPONG_256: e = launch_pingpong(g, s.out, p, st); break;
+        case K_RING8_256:
+        case K_RING4_256: e = launch_ring(g, s.out, p, st); break;
         case K_GEMV: e = launch_gemv(g, s.out, p, st); break;
         case K_GEMV_LDS: e = launch_gemv_lds(g, s.out, p, st); break;
         default: return GEMM_ERR_UNSUPPORTED;
@@ -323,6 +327,8 @@ const char* gemm_bf16_kernel_name(int k) {
         case K_PERSIST_128: return "persist_128";
         case K_SPEC_256: return "spec_256";
         case K_PINGPONG_256: return "pingpong_256";
+        case K_RING8_256: return "ring8_256";
+        case K_RING4_256: return "ring4_256";
         case K_GEMV: return "gemv";
         case K_GEMV_LDS: return "gemv_lds";
         default: return "?";

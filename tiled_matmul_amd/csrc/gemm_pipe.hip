@@ -30,6 +30,7 @@
 // rounded down to a multiple of 8 are turned into out-of-range buffer offsets, which read
 // zeros; the remaining K - K8 < 8 columns enter through one extra k step after the loop.
 #include "launch.hpp"
+#include "mfma_step.hpp"
 
 namespace tmm {
 
@@ -54,79 +55,6 @@ struct PipeCfg {
         else if constexpr (SWZ == 1) return r & (KC - 1);
         else return (r >> 1) & (KC - 1);
     }
-};
-
-// The two bf16 MFMA shapes of gfx950.  ROWS x ROWS output block per instruction, KS = k
-// depth per instruction; lane l supplies row (l % ROWS) and the 8-element k chunk
-// (l / ROWS) of each operand.
-template <int MF>
-struct Mma;
-template <>
-struct Mma<16> {
-    static constexpr int ROWS = 16, KS = 32;
-    typedef f32x4 Acc;
-    static __device__ __forceinline__ Acc run(bf16x8 a, bf16x8 b, Acc c) { return mfma_16x16x32(a, b, c); }
-    static __device__ __forceinline__ Acc zero() { return Acc{0.f, 0.f, 0.f, 0.f}; }
-};
-template <>
-struct Mma<32> {
-    static constexpr int ROWS = 32, KS = 16;
-    typedef f32x16 Acc;
-    static __device__ __forceinline__ Acc run(bf16x8 a, bf16x8 b, Acc c) { return mfma_32x32x16(a, b, c); }
-    static __device__ __forceinline__ Acc zero() {
-        Acc z;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = 0.f;
-        return z;
-    }
-};
-
-// One k step of MFMAs on fragments `f`, with NR fragment reads (rd(q)) and NG load issues
-// (ld(q)) for later steps placed evenly between groups of MFMAs.  sched_barrier fences fix
-// this order: LDS reads issued in one burst fill the LDS command FIFO and, since a wave
-// issues in order, stall the MFMAs queued behind them.
-// FINE = false keeps the reads and loads in one group ahead of the MFMAs (the 4-wave kernel,
-// whose 256 accumulators leave LLVM too few registers to interleave without copies).
-template <int FN, int FM, int NR, int NG, bool FINE, typename Acc, typename F, typename RD, typename LD>
-__device__ __forceinline__ void step(Acc (&acc)[FN][FM], const F& f, RD rd, LD ld) {
-    constexpr int NM = FN * FM;
-    if constexpr (!FINE) {
-#pragma unroll
-        for (int q = 0; q < NR; ++q) rd(q);
-#pragma unroll
-        for (int q = 0; q < NG; ++q) ld(q);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) acc[m / FM][m % FM] = Mma<(sizeof(Acc) == 16 ? 16 : 32)>::run(
-            f.b[m / FM], f.a[m % FM], acc[m / FM][m % FM]);
-        __builtin_amdgcn_sched_barrier(0);
-        return;
-    }
-    constexpr int SLOTS = NR > NG ? NR : NG;
-    static_assert(!FINE || NM >= SLOTS, "needs at least one MFMA per slot");
-#pragma unroll
-    for (int q = 0; q < SLOTS; ++q) {
-        if (q < NR) rd(q);
-        if (q < NG) ld(q);
-        __builtin_amdgcn_sched_barrier(0);
-        constexpr int base = NM / SLOTS, extra = NM % SLOTS;
-        const int m0 = q * base + (q < extra ? q : extra);
-        const int m1 = m0 + base + (q < extra ? 1 : 0);
-#pragma unroll
-        for (int m = m0; m < m1; ++m) {
-            const int i = m / FM, j = m % FM;
-            acc[i][j] = Mma<(sizeof(Acc) == 16 ? 16 : 32)>::run(f.b[i], f.a[j], acc[i][j]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// Register fragments of one k step of a wave: FN fragments of the B tile (the MFMA's first
-// operand) and FM of the A tile (its second).
-template <int FN, int FM>
-struct Frags {
-    bf16x8 b[FN];
-    bf16x8 a[FM];
 };
 
 // RAGGED: K is not a multiple of 8 (a separate instance, so that the common case carries

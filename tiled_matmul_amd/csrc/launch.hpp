@@ -22,7 +22,9 @@ enum KernelId {
     K_GEMV = 9,             // ladder step 6: skinny-M bandwidth path, MFMA form (M <= 16)
     K_GEMV_LDS = 10,        //   same, dot-product form: contiguous W rows, X staged in LDS
     K_PINGPONG_256 = 11,    // ladder steps 7-9: two wave groups alternate load and MFMA phases
-    K_COUNT = 12
+    K_RING8_256 = 12,       // steps 4-6 with a five-slot 32-deep ring, loads spread over the K loop; 8 waves
+    K_RING4_256 = 13,       //   same, 4 waves of 128 x 128 (AGPR accumulators)
+    K_COUNT = 14
 };
 
 // Launch shape chosen for a problem (filled by the planner, consumed by the launchers).
@@ -39,6 +41,7 @@ hipError_t launch_simple(const GemmArgs& g, int out, const Plan& p, hipStream_t 
 hipError_t launch_mfma(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_pingpong(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_ring(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_gemv_lds(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 int gemv_lds_rows_per_workgroup();

@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 output for the committed profiles (host tool, no GPU).
 
-    python -m tiled_matmul_amd.proftools stats <kernel_stats.csv | kernel_trace.csv>
-        per-kernel dispatch count and average / min / max duration (us)
+    python -m tiled_matmul_amd.proftools stats <kernel_trace.csv> [--skip-first N]
+        per-kernel dispatch count and average / min / max duration (us), optionally without
+        each kernel's first N dispatches (the warm-up launches of a timed run)
     python -m tiled_matmul_amd.proftools traffic --fetch F.csv --write W.csv \
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --kernel SUBSTR \
         --workload NAME --sha SHA --out profiles/traffic_<kernel>_<workload>.json
@@ -24,13 +25,14 @@ def _rows(path):
 
 
 def kernel_durations(path):
-    """{kernel name: [duration ns, ...]} from a kernel trace CSV."""
+    """{kernel name: [duration ns, ...] in launch order} from a kernel trace CSV."""
     d = defaultdict(list)
     for r in _rows(path):
         name = r.get("Kernel_Name") or r.get("Name")
         if "Start_Timestamp" in r and "End_Timestamp" in r:
-            d[name].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    return d
+            start, end = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            d[name].append((start, end - start))
+    return {k: [dur for _, dur in sorted(v)] for k, v in d.items()}
 
 
 def counter_per_dispatch(path, counter, substr):
@@ -49,6 +51,7 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("trace")
+    s.add_argument("--skip-first", type=int, default=0)
     t = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--workload",
               "--sha", "--out"):
@@ -58,6 +61,7 @@ def main():
     a = ap.parse_args()
     if a.cmd == "stats":
         for name, v in sorted(kernel_durations(a.trace).items(), key=lambda x: -sum(x[1])):
+            v = v[a.skip_first:] if len(v) > a.skip_first else v
             print(f"| {name[:90]} | {len(v)} | {statistics.mean(v) / 1e3:.2f} | "
                   f"{min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} |")
         return
