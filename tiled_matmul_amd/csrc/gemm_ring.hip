@@ -35,6 +35,16 @@
 
 namespace tmm {
 
+// MFMAs after each k step's last fragment read (see step()); measured on MI355X: 16 for the
+// 4-wave layout (1-2% faster than reads spread to the end of the step; 24-40 no better), 0
+// for the 8-wave layout.
+#ifndef TMM_RING4_TAIL
+#define TMM_RING4_TAIL 16
+#endif
+#ifndef TMM_RING8_TAIL
+#define TMM_RING8_TAIL 0
+#endif
+
 namespace rg {
 constexpr int BM = 256, BN = 256, BK = 64, NA = 3, NB = 2;
 constexpr int ROWB = BK * 2;                        // bytes per LDS row
@@ -52,6 +62,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     using MM = std::conditional_t<ASM, MmaAsm16, Mma<16>>;
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, FM = WM / 16, FN = WN / 16;
+    // MFMAs at the end of each k step that follow the step's last fragment read.
+    constexpr int RTAIL = NW == 4 ? TMM_RING4_TAIL : TMM_RING8_TAIL;
     constexpr int L = 256 / (NW * R);   // load instructions per wave for one A (or B) tile
     static_assert(L * NW * R == 256, "rows split over the waves");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[(NA + NB) * TILE];
@@ -136,11 +148,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         // a0, a1, a2: A slots of blocks b, b+1, b+2; b0, b1: B slots of blocks b, b+1.
         int a0 = 0, a1 = TILE, a2 = 2 * TILE, b0 = B_BASE, b1 = B_BASE + TILE;
         for (int b = 0; b < nk; ++b) {
-            step<FN, FM, FN + FM, L, true, MM>(acc, f[0], [&](int q) { read_one(f[1], q, a0, b0, 1); },
+            step<FN, FM, FN + FM, L, true, MM, RTAIL>(acc, f[0], [&](int q) { read_one(f[1], q, a0, b0, 1); },
                                                [&](int q) { load_one(true, q, b + 2, a2); });
             wait_cnt<L, 0>();   // everything but this step's A(b+2) loads has landed
             barrier();
-            step<FN, FM, FN + FM, L, true, MM>(acc, f[1], [&](int q) { read_one(f[0], q, a1, b1, 0); },
+            step<FN, FM, FN + FM, L, true, MM, RTAIL>(acc, f[1], [&](int q) { read_one(f[0], q, a1, b1, 0); },
                                                [&](int q) { load_one(false, q, b + 2, b0); });
             __builtin_amdgcn_sched_barrier(0);
             wait_cnt<63, 0>();

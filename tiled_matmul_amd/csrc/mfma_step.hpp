@@ -36,14 +36,17 @@ struct Mma<32> {
 };
 
 // One k step of MFMAs on fragments `f`, with NR fragment reads (rd(q)) and NG load issues
-// (ld(q)) for later steps placed evenly between groups of MFMAs.  sched_barrier fences fix
-// this order: LDS reads issued in one burst fill the LDS command FIFO and, since a wave
-// issues in order, stall the MFMAs queued behind them.
-// FINE = false keeps the reads and loads in one group ahead of the MFMAs (the 4-wave kernel,
-// whose 256 accumulators leave LLVM too few registers to interleave without copies).
+// (ld(q)) for later steps placed between the MFMAs.  sched_barrier fences fix this order:
+// LDS reads issued in one burst fill the LDS command FIFO and, since a wave issues in order,
+// stall the MFMAs queued behind them.  With FINE, read q goes before MFMA
+// q (NM - TAIL) / NR, so the last TAIL MFMAs of the step cover the latency of the last reads
+// (the next step waits for all of them), and load q goes before MFMA q NM / NG.
+// FINE = false keeps the reads and loads in one group ahead of the MFMAs (the 4-wave kernel
+// of gemm_pipe.hip, whose 256 builtin accumulators leave LLVM too few registers to
+// interleave without copies).
 // MM: the MFMA policy (default: the builtin shape that matches Acc).
-template <int FN, int FM, int NR, int NG, bool FINE, typename MM = void, typename Acc, typename F, typename RD,
-          typename LD>
+template <int FN, int FM, int NR, int NG, bool FINE, typename MM = void, int TAIL = -1, typename Acc, typename F,
+          typename RD, typename LD>
 __device__ __forceinline__ void step(Acc (&acc)[FN][FM], const F& f, RD rd, LD ld) {
     using M = std::conditional_t<std::is_void_v<MM>, Mma<(sizeof(Acc) == 16 ? 16 : 32)>, MM>;
     constexpr int NM = FN * FM;
@@ -57,23 +60,40 @@ __device__ __forceinline__ void step(Acc (&acc)[FN][FM], const F& f, RD rd, LD l
         for (int m = 0; m < NM; ++m) acc[m / FM][m % FM] = M::run(f.b[m / FM], f.a[m % FM], acc[m / FM][m % FM]);
         __builtin_amdgcn_sched_barrier(0);
         return;
-    }
-    constexpr int SLOTS = NR > NG ? NR : NG;
-    static_assert(!FINE || NM >= SLOTS, "needs at least one MFMA per slot");
+    } else if constexpr (TAIL < 0) {
+        // Slots: max(NR, NG) groups of MFMAs, read q and load q at the head of group q.
+        constexpr int SLOTS = NR > NG ? NR : NG;
+        static_assert(NM >= SLOTS, "needs at least one MFMA per slot");
 #pragma unroll
-    for (int q = 0; q < SLOTS; ++q) {
-        if (q < NR) rd(q);
-        if (q < NG) ld(q);
-        __builtin_amdgcn_sched_barrier(0);
-        constexpr int base = NM / SLOTS, extra = NM % SLOTS;
-        const int m0 = q * base + (q < extra ? q : extra);
-        const int m1 = m0 + base + (q < extra ? 1 : 0);
+        for (int q = 0; q < SLOTS; ++q) {
+            if (q < NR) rd(q);
+            if (q < NG) ld(q);
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int base = NM / SLOTS, extra = NM % SLOTS;
+            const int m0 = q * base + (q < extra ? q : extra);
+            const int m1 = m0 + base + (q < extra ? 1 : 0);
 #pragma unroll
-        for (int m = m0; m < m1; ++m) {
+            for (int m = m0; m < m1; ++m) {
+                const int i = m / FM, j = m % FM;
+                acc[i][j] = M::run(f.b[i], f.a[j], acc[i][j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        static_assert(TAIL < NM, "reads need MFMAs to hide behind");
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+#pragma unroll
+            for (int q = 0; q < NR; ++q)
+                if (q * (NM - TAIL) / NR == m) rd(q);
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+                if (q * NM / NG == m) ld(q);
+            __builtin_amdgcn_sched_barrier(0);
             const int i = m / FM, j = m % FM;
             acc[i][j] = M::run(f.b[i], f.a[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
