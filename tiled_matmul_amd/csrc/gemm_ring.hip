@@ -55,13 +55,19 @@ static_assert((NA + NB) * TILE <= 160 * 1024, "LDS capacity");
 __device__ __forceinline__ int swz(int r) { return r & 7; }
 }  // namespace rg
 
-template <int OUT, bool RAGGED, int WAVES_M, int WAVES_N, bool ASM>
+// MF: MFMA shape (16: v_mfma_f32_16x16x32_bf16, one per 32-deep k step and accumulator;
+// 32: v_mfma_f32_32x32x16_bf16, two per k step).
+template <int OUT, bool RAGGED, int WAVES_M, int WAVES_N, bool ASM, int MF>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void gemm_ring_kernel(
     GemmArgs g, TileGrid tg, int vec_store) {
     using namespace rg;
-    using MM = std::conditional_t<ASM, MmaAsm16, Mma<16>>;
+    using MM = std::conditional_t<MF == 16, std::conditional_t<ASM, MmaAsm16, Mma<16>>,
+                                  std::conditional_t<ASM, MmaAsm32, Mma<32>>>;
+    using Acc = typename MM::Acc;
+    constexpr int KH = 32 / MM::KS;             // MFMAs per accumulator per 32-deep k step
+    constexpr int CPM = MM::KS / 8;             // 16-byte k chunks per MFMA operand row
     constexpr int NW = WAVES_M * WAVES_N;
-    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, FM = WM / 16, FN = WN / 16;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, FM = WM / MF, FN = WN / MF;
     // MFMAs at the end of each k step that follow the step's last fragment read.
     constexpr int RTAIL = NW == 4 ? TMM_RING4_TAIL : TMM_RING8_TAIL;
     constexpr int L = 256 / (NW * R);   // load instructions per wave for one A (or B) tile
@@ -79,12 +85,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     // lane / 8 for every i.
     const int lrow = lane / 8;
     const uint32_t chunk_k = 8u * static_cast<uint32_t>((lane % 8) ^ swz(lrow));
-    // Fragment reads of k step kk: row lane % 16 of a 16-row block, logical chunk
-    // 4 kk + lane / 16.
-    int rd[2];
+    // Fragment reads of sub-step h of k step kk: row lane % MF of an MF-row block, logical
+    // chunk 4 kk + CPM h + lane / MF.
+    int rd[2][KH];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
-        rd[kk] = (lane & 15) * ROWB + (((4 * kk + (lane >> 4)) ^ swz(lane & 15)) * 16);
+#pragma unroll
+        for (int h = 0; h < KH; ++h)
+            rd[kk][h] = (lane % MF) * ROWB + (((4 * kk + CPM * h + lane / MF) ^ swz(lane % MF)) * 16);
     const int a_off = wm * WM * ROWB, b_off = wn * WN * ROWB;
 
     for (int t = blockIdx.x; t < tg.total; t += gridDim.x) {
@@ -112,20 +120,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
             load_lds_16(is_a ? ra : rb, lds + dst + (NW * q + w) * R * ROWB, ok ? (is_a ? va[q] : vb[q]) : OOB,
                         2u * k0);
         };
-        // Fragment q (q < FN: B fragment q, else A fragment q - FN) of k step kk from the
-        // A tile at `at` and the B tile at `bt_`.
-        auto read_one = [&](Frags<FN, FM>& f, int q, int at, int bt_, int kk) {
-            if (q < FN)
-                f.b[q] = *reinterpret_cast<const bf16x8*>(lds + bt_ + b_off + 16 * q * ROWB + rd[kk]);
-            else
-                f.a[q - FN] = *reinterpret_cast<const bf16x8*>(lds + at + a_off + 16 * (q - FN) * ROWB + rd[kk]);
+        // Fragment q of k step kk from the A tile at `at` and the B tile at `bt_`: q < KH FN:
+        // B fragment q % FN of sub-step q / FN, else A fragment (q - KH FN) % FM of sub-step
+        // (q - KH FN) / FM.
+        using F = Frags<KH * FN, KH * FM>;
+        auto read_one = [&](F& f, int q, int at, int bt_, int kk) {
+            if (q < KH * FN) {
+                const int h = q / FN, i = q % FN;
+                f.b[q] = *reinterpret_cast<const bf16x8*>(lds + bt_ + b_off + MF * i * ROWB + rd[kk][h]);
+            } else {
+                const int r = q - KH * FN, h = r / FM, j = r % FM;
+                f.a[r] = *reinterpret_cast<const bf16x8*>(lds + at + a_off + MF * j * ROWB + rd[kk][h]);
+            }
         };
+        constexpr int NR = KH * (FN + FM);
 
-        f32x4 acc[FN][FM];
+        Acc acc[FN][FM];
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < FM; ++j) acc[i][j] = MM::zero();
         if constexpr (ASM) agpr_fence(acc);
 
         // Prologue: A(0), B(0), A(1), B(1); block 0 complete (this wave), barrier (every
@@ -140,19 +154,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         }
         wait_vmcnt<2 * L>();
         barrier();
-        Frags<FN, FM> f[2];
+        F f[2];
 #pragma unroll
-        for (int q = 0; q < FN + FM; ++q) read_one(f[0], q, 0, B_BASE, 0);
+        for (int q = 0; q < NR; ++q) read_one(f[0], q, 0, B_BASE, 0);
         wait_cnt<63, 0>();
 
         // a0, a1, a2: A slots of blocks b, b+1, b+2; b0, b1: B slots of blocks b, b+1.
         int a0 = 0, a1 = TILE, a2 = 2 * TILE, b0 = B_BASE, b1 = B_BASE + TILE;
         for (int b = 0; b < nk; ++b) {
-            step<FN, FM, FN + FM, L, true, MM, RTAIL>(acc, f[0], [&](int q) { read_one(f[1], q, a0, b0, 1); },
+            step<FN, FM, NR, L, true, MM, RTAIL>(acc, f[0], [&](int q) { read_one(f[1], q, a0, b0, 1); },
                                                [&](int q) { load_one(true, q, b + 2, a2); });
             wait_cnt<L, 0>();   // everything but this step's A(b+2) loads has landed
             barrier();
-            step<FN, FM, FN + FM, L, true, MM, RTAIL>(acc, f[1], [&](int q) { read_one(f[0], q, a1, b1, 0); },
+            step<FN, FM, NR, L, true, MM, RTAIL>(acc, f[1], [&](int q) { read_one(f[0], q, a1, b1, 0); },
                                                [&](int q) { load_one(false, q, b + 2, b0); });
             __builtin_amdgcn_sched_barrier(0);
             wait_cnt<63, 0>();
@@ -188,41 +202,55 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
             }
             barrier();
 #pragma unroll
-            for (int q = 0; q < FN + FM; ++q) read_one(f[0], q, 0, B_BASE, 0);
+            for (int q = 0; q < NR; ++q) read_one(f[0], q, 0, B_BASE, 0);
             wait_cnt<63, 0>();
 #pragma unroll
-            for (int i = 0; i < FN; ++i)
+            for (int h = 0; h < KH; ++h)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) acc[i][j] = MM::run(f[0].b[i], f[0].a[j], acc[i][j]);
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) acc[i][j] = MM::run(f[0].b[h * FN + i], f[0].a[h * FM + j], acc[i][j]);
             barrier();   // read before the next tile refills the rings
         }
         if constexpr (ASM) agpr_fence(acc);
 
         void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
                                   : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
-        store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
+        if constexpr (MF == 16)
+            store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
+        else
+            store_acc32<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
     }
 }
 
-template <int WM, int WN, bool ASM>
+template <int WM, int WN, bool ASM, int MF>
 static hipError_t launch_ring_cfg(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
     const bool ragged = (g.K & 7) != 0;
     const dim3 grid(p.grid_x), block(64 * WM * WN);
     if (out == OUT_F32 && ragged)
-        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, true, WM, WN, ASM>), grid, block, 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, true, WM, WN, ASM, MF>), grid, block, 0, s, g, p.grid, p.vec_store);
     else if (out == OUT_F32)
-        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, false, WM, WN, ASM>), grid, block, 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, false, WM, WN, ASM, MF>), grid, block, 0, s, g, p.grid, p.vec_store);
     else if (ragged)
-        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, true, WM, WN, ASM>), grid, block, 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, true, WM, WN, ASM, MF>), grid, block, 0, s, g, p.grid, p.vec_store);
     else
-        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, false, WM, WN, ASM>), grid, block, 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, false, WM, WN, ASM, MF>), grid, block, 0, s, g, p.grid, p.vec_store);
     return hipGetLastError();
 }
 
+// MFMA shape of the ring kernels (16 or 32; v_mfma_f32_32x32x16_bf16 measured 5-7% slower on
+// MI355X for both layouts).
+#ifndef TMM_RING4_MFMA
+#define TMM_RING4_MFMA 16
+#endif
+#ifndef TMM_RING8_MFMA
+#define TMM_RING8_MFMA 16
+#endif
+
 hipError_t launch_ring(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
     switch (p.kernel) {
-        case K_RING8_256: return launch_ring_cfg<2, 4, false>(g, out, p, s);
-        case K_RING4_256: return launch_ring_cfg<2, 2, true>(g, out, p, s);
+        case K_RING8_256: return launch_ring_cfg<2, 4, false, TMM_RING8_MFMA>(g, out, p, s);
+        case K_RING4_256: return launch_ring_cfg<2, 2, true, TMM_RING4_MFMA>(g, out, p, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -80,18 +80,22 @@ __device__ __forceinline__ void step(Acc (&acc)[FN][FM], const F& f, RD rd, LD l
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
-        static_assert(TAIL < NM, "reads need MFMAs to hide behind");
+        // f may hold KH sub-steps of fragments (b[KH FN], a[KH FM]): MFMA m uses sub-step
+        // m / (FN FM).
+        constexpr int KH = static_cast<int>(sizeof(f.b) / sizeof(f.b[0])) / FN;
+        constexpr int NMK = NM * KH;
+        static_assert(TAIL < NMK, "reads need MFMAs to hide behind");
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
+        for (int m = 0; m < NMK; ++m) {
 #pragma unroll
             for (int q = 0; q < NR; ++q)
-                if (q * (NM - TAIL) / NR == m) rd(q);
+                if (q * (NMK - TAIL) / NR == m) rd(q);
 #pragma unroll
             for (int q = 0; q < NG; ++q)
-                if (q * NM / NG == m) ld(q);
+                if (q * NMK / NG == m) ld(q);
             __builtin_amdgcn_sched_barrier(0);
-            const int i = m / FM, j = m % FM;
-            acc[i][j] = M::run(f.b[i], f.a[j], acc[i][j]);
+            const int h = m / NM, i = (m % NM) / FM, j = m % FM;
+            acc[i][j] = M::run(f.b[h * FN + i], f.a[h * FM + j], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -119,6 +123,17 @@ struct MmaAsm16 {
         return c;
     }
     static __device__ __forceinline__ Acc zero() { return Acc{0.f, 0.f, 0.f, 0.f}; }
+};
+
+// v_mfma_f32_32x32x16_bf16 the same way (16 AGPRs per accumulator).
+struct MmaAsm32 {
+    static constexpr int ROWS = 32, KS = 16;
+    typedef f32x16 Acc;
+    static __device__ __forceinline__ Acc run(bf16x8 a, bf16x8 b, Acc c) {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+        return c;
+    }
+    static __device__ __forceinline__ Acc zero() { return Mma<32>::zero(); }
 };
 
 // Every accumulator passes through an empty assembly statement before and after 24 wait
