@@ -60,7 +60,7 @@ def to_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def make_sets(name, torch, min_bytes):
+def make_sets(name, torch, min_bytes, la=0, lb=0):
     """Enough copies of the workload's operands (and outputs) to exceed min_bytes.  Device
     operands are (M, K) and (N, K), or (batch, M, K) and (batch, N, K) for a batched
     workload; the host arrays returned are batch item 0's."""
@@ -73,6 +73,11 @@ def make_sets(name, torch, min_bytes):
     else:
         Ad = to_dev(np.stack([a for a, _ in items]), torch)
         Bd = to_dev(np.stack([b for _, b in items]), torch)
+    # MN-major operands: the same values stored transposed (K x M, K x N)
+    if la == tm.GEMM_LAYOUT_MN_MAJOR:
+        Ad = Ad.transpose(-1, -2).contiguous()
+    if lb == tm.GEMM_LAYOUT_MN_MAJOR:
+        Bd = Bd.transpose(-1, -2).contiguous()
     out_t = torch.float32 if out == tm.GEMM_OUT_FP32 else torch.bfloat16
     cshape = (M, N) if batch == 1 else (batch, M, N)
     per = Ad.numel() * 2 + Bd.numel() * 2 + batch * M * N * (4 if out == tm.GEMM_OUT_FP32 else 2)
@@ -118,18 +123,22 @@ def gemm_leg(args, torch):
     w = synth.WORKLOADS[name]
     M, N, K, out, batch = w["M"], w["N"], w["K"], w["out"], w["batch"]
     sA, sB, sC = (M * K, N * K, M * N) if batch > 1 else (0, 0, 0)
+    la = tm.GEMM_LAYOUT_MN_MAJOR if args.a_layout == "mn" else tm.GEMM_LAYOUT_K_MAJOR
+    lb = tm.GEMM_LAYOUT_MN_MAJOR if args.b_layout == "mn" else tm.GEMM_LAYOUT_K_MAJOR
+    lda = M if la == tm.GEMM_LAYOUT_MN_MAJOR else K
+    ldb = N if lb == tm.GEMM_LAYOUT_MN_MAJOR else K
     log(f"[bench] generating {name} operands")
-    (A, B), sets = make_sets(name, torch, args.rotate_mb * 2 ** 20)
+    (A, B), sets = make_sets(name, torch, args.rotate_mb * 2 ** 20, la, lb)
     variant = tm.VARIANTS[args.variant]
-    rc, kname, grid, block = tm.gemm_bf16_plan(variant, batch, M, N, K, sets[0][0], K, sA,
-                                               sets[0][1], K, sB, sets[0][2], N, sC, out,
-                                               torch.cuda.get_device_properties(0).multi_processor_count)
+    rc, kname, grid, block = tm.gemm_bf16_layout_plan(
+        la, lb, variant, batch, M, N, K, sets[0][0], lda, sA, sets[0][1], ldb, sB, sets[0][2], N,
+        sC, out, torch.cuda.get_device_properties(0).multi_processor_count)
     if rc != 0:
         raise SystemExit(f"variant {args.variant} cannot run {name}: {tm.gemm_bf16_status_string(rc)}")
 
     def launch(i):
         a, b, c = sets[i]
-        tm.gemm_bf16_variant(variant, batch, M, N, K, a, K, sA, b, K, sB, c, N, sC, out)
+        tm.gemm_bf16_layout(la, lb, variant, batch, M, N, K, a, lda, sA, b, ldb, sB, c, N, sC, out)
 
     log(f"[bench] timing {name}: kernel {kname}, {len(sets)} rotating buffer sets, "
         f"{args.warmup} warm-up + {args.steps} timed steps")
@@ -140,6 +149,7 @@ def gemm_leg(args, torch):
     nbytes = batch * rl.algorithmic_bytes(M, N, K, obytes)
     return {
         "name": name, "batch": batch, "M": M, "N": N, "K": K,
+        "layouts": f"A {args.a_layout}-major, B {args.b_layout}-major",
         "out": "fp32" if out == 0 else "bf16",
         "kernel": kname, "grid": grid, "block": block, "ms": ms, "wall_s": wall,
         "tflops": tflops, "flops": flops, "bytes": nbytes, "A": A, "B": B, "sets": sets,
@@ -274,6 +284,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square_4096", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--variant", default="auto", choices=sorted(tm.VARIANTS))
+    ap.add_argument("--a-layout", default="k", choices=["k", "mn"],
+                    help="A stored M x K (k) or K x M (mn)")
+    ap.add_argument("--b-layout", default="k", choices=["k", "mn"],
+                    help="B stored N x K (k) or K x N (mn: C = A B)")
     ap.add_argument("--rotate-mb", type=int, default=512,
                     help="total size of the rotating input/output sets")
     ap.add_argument("--gemv-workload", default="gemv_m1", choices=["gemv_m1", "gemv_m16"],
@@ -318,7 +332,7 @@ def main():
                                + (f"batch={res['batch']} " if res["batch"] > 1 else "")
                                + f"M={res['M']} N={res['N']} K={res['K']}, bf16 in, "
                                f"fp32 accumulate, {res['out']} out",
-                   "variant": args.variant, "kernel": res["kernel"],
+                   "layouts": res["layouts"], "variant": args.variant, "kernel": res["kernel"],
                    "grid": res["grid"], "block": res["block"],
                    "rotating_buffer_sets": len(res["sets"])},
         "pct_mfma_peak": 100.0 * res["tflops"] / MFMA_TFLOPS,

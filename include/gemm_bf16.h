@@ -63,8 +63,20 @@ extern "C" {
 #define GEMM_VARIANT_SPECIALIZED 5 /* steps 7-9: producer/consumer waves sharing the B tile    */
 #define GEMM_VARIANT_GEMV 6        /* skinny M (M <= 16): bandwidth-bound decode path         */
 #define GEMM_VARIANT_PINGPONG 7    /* steps 7-9: two wave groups alternate load / MFMA phases  */
-#define GEMM_VARIANT_RING8 8       /* steps 4-6, 5-slot ring of 32-deep K sub-blocks, 8 waves  */
+#define GEMM_VARIANT_RING8 8       /* steps 4-6, separate A and B rings, loads spread, 8 waves */
 #define GEMM_VARIANT_RING4 9       /* the same with 4 waves of 128x128 register tiles          */
+
+/* Operand layouts (gemm_bf16_layout).  The page "读书笔记-《面向机器学习系统的现代 GPU
+ * 编程》", section "三个核心概念：scope、layout、dispatch", names the two ways a GEMM
+ * operand can be stored: contiguous along the reduction dimension (k-major) or along the
+ * output dimension (mn-major).
+ *   GEMM_LAYOUT_K_MAJOR   A(i, k) = A[i * lda + k] (A is M x K), B(j, k) = B[j * ldb + k]
+ *                         (B is N x K): pitch >= K.  What every other entry point takes.
+ *   GEMM_LAYOUT_MN_MAJOR  A(i, k) = A[k * lda + i] (A is stored K x M, pitch >= M),
+ *                         B(j, k) = B[k * ldb + j] (B stored K x N, pitch >= N): with an
+ *                         MN-major B, C = A * B for a row-major K x N matrix B. */
+#define GEMM_LAYOUT_K_MAJOR 0
+#define GEMM_LAYOUT_MN_MAJOR 1
 
 /*
  * C = A * B^T for one problem (definition above).
@@ -136,6 +148,42 @@ int gemm_bf16_plan(int variant, int64_t batch, int64_t M, int64_t N, int64_t K,
                    const void* C, int64_t ldc, int64_t strideC,
                    int out_dtype, int num_cus,
                    int* kernel_id, int64_t* grid_x, int* block);
+
+/*
+ * C[i][j] = sum_k A(i, k) * B(j, k) with each operand in the layout a_layout / b_layout
+ * (GEMM_LAYOUT_*), through kernel variant `variant` (GEMM_VARIANT_AUTO to let the library
+ * choose); otherwise as gemm_bf16_variant: same pointers, strides, output, streams and
+ * status codes, C row-major with pitch ldc, batch items strideA / strideB / strideC
+ * elements apart.  With both layouts K-major this is gemm_bf16_variant.  With an MN-major
+ * operand, AUTO runs the ring kernel (4 waves, 256 x 256 tiles) when A and B are 4-byte
+ * aligned with even pitches and strides and the MN-major operand's extent (M for A, N for
+ * B) is a multiple of 8, and the general 64 x 64 kernel otherwise; of the forced variants
+ * only GEMM_VARIANT_SIMPLE and GEMM_VARIANT_RING4 accept MN-major operands (others return
+ * GEMM_ERR_UNSUPPORTED).  An unknown layout returns GEMM_ERR_ARG.
+ */
+int gemm_bf16_layout(int a_layout, int b_layout, int variant, int64_t batch,
+                     int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda, int64_t strideA,
+                     const void* B, int64_t ldb, int64_t strideB,
+                     void* C, int64_t ldc, int64_t strideC,
+                     int out_dtype, void* stream);
+
+/* gemm_bf16_validate for gemm_bf16_layout's arguments (host-only). */
+int gemm_bf16_layout_validate(int a_layout, int b_layout, int64_t batch,
+                              int64_t M, int64_t N, int64_t K,
+                              const void* A, int64_t lda, int64_t strideA,
+                              const void* B, int64_t ldb, int64_t strideB,
+                              const void* C, int64_t ldc, int64_t strideC,
+                              int out_dtype);
+
+/* gemm_bf16_plan for gemm_bf16_layout's arguments (host-only). */
+int gemm_bf16_layout_plan(int a_layout, int b_layout, int variant, int64_t batch,
+                          int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t lda, int64_t strideA,
+                          const void* B, int64_t ldb, int64_t strideB,
+                          const void* C, int64_t ldc, int64_t strideC,
+                          int out_dtype, int num_cus,
+                          int* kernel_id, int64_t* grid_x, int* block);
 
 /* Name of a kernel id from gemm_bf16_plan ("?" if unknown).  Static storage. */
 const char* gemm_bf16_kernel_name(int kernel_id);

@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tm.gemm_bf16_version() == 3
+    assert tm.gemm_bf16_version() == 4
     for s in range(7):
         assert tm.gemm_bf16_status_string(s).startswith("GEMM_")
     assert tm.gemm_bf16_status_string(99) == "unknown status"
@@ -137,3 +137,55 @@ def test_calls_fail_cleanly_without_gfx950():
     lib = tm.library()
     assert lib.gemm_bf16(64, 64, 64, P, 64, P, 64, P, 64, 0, None) == tm.GEMM_ERR_ARCH
     assert lib.gemm_bf16(64, 64, 64, P, 63, P, 64, P, 64, 0, None) == tm.GEMM_ERR_ARG
+
+
+def lplan(la, lb, variant=0, M=4096, N=4096, K=4096, A=P, lda=None, B=P, ldb=None, out=0, batch=1,
+          sA=0, sB=0, sC=0):
+    lda = (K if la == 0 else M) if lda is None else lda
+    ldb = (K if lb == 0 else N) if ldb is None else ldb
+    return tm.gemm_bf16_layout_plan(la, lb, variant, batch, M, N, K, A, lda, sA, B, ldb, sB, P, N,
+                                    sC, out, 256)
+
+
+def test_layout_validation():
+    MN, KM = tm.GEMM_LAYOUT_MN_MAJOR, tm.GEMM_LAYOUT_K_MAJOR
+    v = tm.gemm_bf16_layout_validate
+    # MN-major A: pitch counts M (here K > M, so lda = M is fine and lda = K is not needed)
+    assert v(MN, KM, 1, 100, 50, 300, P, 100, 0, P, 300, 0, P, 50, 0, 0) == tm.GEMM_OK
+    assert v(MN, KM, 1, 100, 50, 300, P, 99, 0, P, 300, 0, P, 50, 0, 0) == tm.GEMM_ERR_ARG
+    # K-major A needs lda >= K
+    assert v(KM, KM, 1, 100, 50, 300, P, 100, 0, P, 300, 0, P, 50, 0, 0) == tm.GEMM_ERR_ARG
+    # MN-major B: pitch counts N
+    assert v(KM, MN, 1, 100, 50, 300, P, 300, 0, P, 50, 0, P, 50, 0, 0) == tm.GEMM_OK
+    assert v(KM, MN, 1, 100, 50, 300, P, 300, 0, P, 49, 0, P, 50, 0, 0) == tm.GEMM_ERR_ARG
+    assert v(2, KM, 1, 100, 50, 300, P, 300, 0, P, 300, 0, P, 50, 0, 0) == tm.GEMM_ERR_ARG
+    assert v(KM, -1, 1, 100, 50, 300, P, 300, 0, P, 300, 0, P, 50, 0, 0) == tm.GEMM_ERR_ARG
+    # both K-major: the same answers as gemm_bf16_validate
+    assert v(KM, KM, 1, 64, 64, 64, P, 64, 0, P, 64, 0, P, 64, 0, 0) == tm.GEMM_OK
+
+
+def test_layout_plan():
+    MN, KM = tm.GEMM_LAYOUT_MN_MAJOR, tm.GEMM_LAYOUT_K_MAJOR
+    assert lplan(KM, KM)[:2] == (0, "ring4_256")
+    assert lplan(KM, MN)[:2] == (0, "ring4_256")
+    assert lplan(MN, KM)[:2] == (0, "ring4_256")
+    assert lplan(MN, MN)[:2] == (0, "ring4_256")
+    assert lplan(KM, MN)[3] == 256
+    # small shapes still take the ring kernel (tile count is not a precondition)
+    assert lplan(KM, MN, M=64, N=64, K=64)[:2] == (0, "ring4_256")
+    # MN-major extent not a multiple of 8, odd pitch, 2-byte aligned pointer: general kernel
+    assert lplan(MN, KM, M=4095)[:2] == (0, "simple_64")
+    assert lplan(KM, MN, N=4093)[:2] == (0, "simple_64")
+    assert lplan(KM, MN, ldb=4097)[:2] == (0, "simple_64")
+    assert lplan(KM, MN, B=P + 2)[:2] == (0, "simple_64")
+    # forced variants
+    assert lplan(KM, MN, variant=1)[:2] == (0, "simple_64")
+    assert lplan(KM, MN, variant=9)[:2] == (0, "ring4_256")
+    assert lplan(KM, MN, variant=9, N=4093)[0] == tm.GEMM_ERR_UNSUPPORTED
+    for variant in (2, 3, 4, 5, 6, 7, 8):
+        assert lplan(KM, MN, variant=variant)[0] == tm.GEMM_ERR_UNSUPPORTED, variant
+    assert lplan(KM, MN, variant=10)[0] == tm.GEMM_ERR_ARG
+    # K = 0: zero fill in any layout
+    assert lplan(MN, MN, K=0, lda=4096, ldb=4096)[:2] == (0, "zero_fill")
+    # both K-major: the K-major planner (the GEMV path included)
+    assert lplan(KM, KM, M=1)[:2] == (0, "gemv_lds")

@@ -32,6 +32,9 @@ GEMM_ERR_UNSUPPORTED = 6
 GEMM_OUT_FP32 = 0
 GEMM_OUT_BF16 = 1
 
+GEMM_LAYOUT_K_MAJOR = 0
+GEMM_LAYOUT_MN_MAJOR = 1
+
 GEMM_VARIANT_AUTO = 0
 GEMM_VARIANT_SIMPLE = 1
 GEMM_VARIANT_MFMA = 2
@@ -79,8 +82,13 @@ def _load():
     lib.gemm_bf16_validate.argtypes = batched
     lib.gemm_bf16_plan.argtypes = [_int] + batched + [_int, ctypes.POINTER(_int),
                                                       ctypes.POINTER(_i64), ctypes.POINTER(_int)]
+    lib.gemm_bf16_layout.argtypes = [_int, _int, _int] + batched + [_vp]
+    lib.gemm_bf16_layout_validate.argtypes = [_int, _int] + batched
+    lib.gemm_bf16_layout_plan.argtypes = [_int, _int, _int] + batched + [
+        _int, ctypes.POINTER(_int), ctypes.POINTER(_i64), ctypes.POINTER(_int)]
     for f in ("gemm_bf16", "gemm_bf16_strided_batched", "gemm_bf16_variant",
-              "gemm_bf16_validate", "gemm_bf16_plan", "gemm_bf16_version"):
+              "gemm_bf16_validate", "gemm_bf16_plan", "gemm_bf16_version", "gemm_bf16_layout",
+              "gemm_bf16_layout_validate", "gemm_bf16_layout_plan"):
         getattr(lib, f).restype = _int
     lib.gemm_bf16_kernel_name.argtypes = [_int]
     lib.gemm_bf16_kernel_name.restype = ctypes.c_char_p
@@ -161,6 +169,31 @@ def gemm_bf16_plan(variant, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C,
     rc = _load().gemm_bf16_plan(variant, batch, M, N, K, _ptr(A), lda, strideA, _ptr(B), ldb,
                                 strideB, _ptr(C), ldc, strideC, out_dtype, num_cus,
                                 ctypes.byref(k), ctypes.byref(g), ctypes.byref(b))
+    return rc, gemm_bf16_kernel_name(k.value), g.value, b.value
+
+
+def gemm_bf16_layout(a_layout, b_layout, variant, batch, M, N, K, A, lda, strideA, B, ldb, strideB,
+                     C, ldc, strideC, out_dtype, stream=None):
+    _check(_load().gemm_bf16_layout(a_layout, b_layout, variant, batch, M, N, K, _ptr(A), lda,
+                                    strideA, _ptr(B), ldb, strideB, _ptr(C), ldc, strideC,
+                                    out_dtype, _stream(stream)), "gemm_bf16_layout")
+
+
+def gemm_bf16_layout_validate(a_layout, b_layout, batch, M, N, K, A, lda, strideA, B, ldb,
+                              strideB, C, ldc, strideC, out_dtype) -> int:
+    return _load().gemm_bf16_layout_validate(a_layout, b_layout, batch, M, N, K, _ptr(A), lda,
+                                             strideA, _ptr(B), ldb, strideB, _ptr(C), ldc,
+                                             strideC, out_dtype)
+
+
+def gemm_bf16_layout_plan(a_layout, b_layout, variant, batch, M, N, K, A, lda, strideA, B, ldb,
+                          strideB, C, ldc, strideC, out_dtype, num_cus=0):
+    """(status, kernel_name, workgroups, threads_per_workgroup)."""
+    k, g, b = _int(0), _i64(0), _int(0)
+    rc = _load().gemm_bf16_layout_plan(a_layout, b_layout, variant, batch, M, N, K, _ptr(A), lda,
+                                       strideA, _ptr(B), ldb, strideB, _ptr(C), ldc, strideC,
+                                       out_dtype, num_cus, ctypes.byref(k), ctypes.byref(g),
+                                       ctypes.byref(b))
     return rc, gemm_bf16_kernel_name(k.value), g.value, b.value
 
 

@@ -16,7 +16,9 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 enum { OUT_F32 = 0, OUT_BF16 = 1 };
 
 // Problem description handed to every kernel by value.  Pointers are device pointers;
-// leading dimensions and batch strides are in elements.
+// leading dimensions and batch strides are in elements.  la / lb: operand layouts
+// (LAYOUT_K: element (i, k) at i * ld + k; LAYOUT_MN: at k * ld + i).
+enum { LAYOUT_K = 0, LAYOUT_MN = 1 };
 struct GemmArgs {
     int64_t batch, M, N, K;
     const uint16_t* A;
@@ -25,6 +27,7 @@ struct GemmArgs {
     int64_t ldb, sB;
     void* C;
     int64_t ldc, sC;
+    int la = LAYOUT_K, lb = LAYOUT_K;
 };
 
 // Tile grid of one launch: tiles_m x tiles_n tiles per batch item, `total` over the batch.

@@ -11,7 +11,7 @@ using namespace tmm;
 
 namespace {
 
-constexpr int kVersion = 3;
+constexpr int kVersion = 4;
 constexpr int kDefaultCUs = 256;        // MI355X
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t k2G = int64_t(1) << 31;
@@ -48,15 +48,22 @@ int current_device(int* cus) {
 }
 
 // --- validation --------------------------------------------------------------------------
-int validate(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+// la / lb: GEMM_LAYOUT_K_MAJOR (element (i, k) at i * ld + k: ld >= K) or
+// GEMM_LAYOUT_MN_MAJOR (at k * ld + i: ld >= M for A, >= N for B).
+int validate(int la, int lb, int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
              int64_t sA, const void* B, int64_t ldb, int64_t sB, const void* C, int64_t ldc,
              int64_t sC, int out) {
     if (out != GEMM_OUT_FP32 && out != GEMM_OUT_BF16) return GEMM_ERR_DTYPE;
+    if ((la != GEMM_LAYOUT_K_MAJOR && la != GEMM_LAYOUT_MN_MAJOR) ||
+        (lb != GEMM_LAYOUT_K_MAJOR && lb != GEMM_LAYOUT_MN_MAJOR))
+        return GEMM_ERR_ARG;
     if (batch < 0 || batch > kMaxBatch || M < 0 || N < 0 || K < 0) return GEMM_ERR_ARG;
     const int64_t big = int64_t(1) << 40;   // keeps every index product inside int64
     if (M > big || N > big || K > big || lda > big || ldb > big || ldc > big) return GEMM_ERR_ARG;
     if (sA > big || sB > big || sC > big) return GEMM_ERR_ARG;
-    if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1)) return GEMM_ERR_ARG;
+    const int64_t need_a = la == GEMM_LAYOUT_K_MAJOR ? K : M, need_b = lb == GEMM_LAYOUT_K_MAJOR ? K : N;
+    if (lda < (need_a > 1 ? need_a : 1) || ldb < (need_b > 1 ? need_b : 1) || ldc < (N > 1 ? N : 1))
+        return GEMM_ERR_ARG;
     if (sA < 0 || sB < 0 || sC < 0) return GEMM_ERR_ARG;
     if (batch == 0 || M == 0 || N == 0) return GEMM_OK;
     if (batch > 1 && sC < (M - 1) * ldc + N) return GEMM_ERR_ARG;
@@ -75,6 +82,7 @@ struct Shape {
     int64_t batch, M, N, K, lda, sA, ldb, sB, ldc, sC;
     const void *A, *B, *C;
     int out;
+    int la = GEMM_LAYOUT_K_MAJOR, lb = GEMM_LAYOUT_K_MAJOR;
 };
 
 // The ping-pong kernel: 16-byte aligned rows, 16-byte chunks that never straddle K, 32-bit
@@ -154,7 +162,9 @@ int plan_pipe(const Shape& s, bool persistent, int cus, Plan& p) {
 // `kernel`: K_SPEC_256 (both groups load and multiply in lockstep) or K_PINGPONG_256 (the
 // groups alternate load and MFMA phases).
 int plan_spec(const Shape& s, int cus, Plan& p, int kernel = K_SPEC_256) {
-    if (kernel == K_PINGPONG_256 ? !fast_loads_ok(s, 256) : !pipe_loads_ok(s, 256)) return GEMM_ERR_UNSUPPORTED;
+    const bool kmajor = s.la == GEMM_LAYOUT_K_MAJOR && s.lb == GEMM_LAYOUT_K_MAJOR;
+    if (kmajor && (kernel == K_PINGPONG_256 ? !fast_loads_ok(s, 256) : !pipe_loads_ok(s, 256)))
+        return GEMM_ERR_UNSUPPORTED;
     tile_grid(s, 256, 256, p);
     p.kernel = kernel;
     p.grid_x = std::min(p.grid.total, cus);
@@ -192,6 +202,33 @@ int plan_gemv(const Shape& s, Plan& p) {
     return GEMM_OK;
 }
 
+// The ring kernel with MN-major operands: 4-byte aligned rows with even pitches (as for the
+// K-major kernels), an MN-major operand's extent (M or N) a multiple of 8 (whole 16-byte
+// chunks) and all of its rows within 32-bit buffer offsets.
+bool ring_layout_ok(const Shape& s) {
+    if (!aligned(s.A, 4) || !aligned(s.B, 4) || s.lda % 2 || s.ldb % 2) return false;
+    if (s.batch > 1 && (s.sA % 2 || s.sB % 2)) return false;
+    auto op_ok = [&](int lay, int64_t ld, int64_t ext) {
+        if (lay == GEMM_LAYOUT_K_MAJOR) return 256 * ld * 2 < k2G;
+        return ext % 8 == 0 && ((s.K - 1) * ld + ext) * 2 < k2G;
+    };
+    return op_ok(s.la, s.lda, s.M) && op_ok(s.lb, s.ldb, s.N);
+}
+
+// MN-major operands: AUTO takes the ring kernel (4 waves) where its preconditions hold and
+// the simple kernel otherwise; of the forced variants only those two take such operands.
+int plan_layout(int variant, const Shape& s, int cus, Plan& p) {
+    switch (variant) {
+        case GEMM_VARIANT_SIMPLE: return plan_2d(s, K_SIMPLE_64, 64, p);
+        case GEMM_VARIANT_RING4:
+            return ring_layout_ok(s) ? plan_spec(s, cus, p, K_RING4_256) : GEMM_ERR_UNSUPPORTED;
+        case GEMM_VARIANT_AUTO:
+            if (ring_layout_ok(s) && plan_spec(s, cus, p, K_RING4_256) == GEMM_OK) return GEMM_OK;
+            return plan_2d(s, K_SIMPLE_64, 64, p) == GEMM_OK ? GEMM_OK : GEMM_ERR_ARG;
+        default: return GEMM_ERR_UNSUPPORTED;
+    }
+}
+
 int make_plan(int variant, const Shape& s, int cus, Plan& p) {
     if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_RING4) return GEMM_ERR_ARG;
     p = Plan{};
@@ -206,6 +243,7 @@ int make_plan(int variant, const Shape& s, int cus, Plan& p) {
         p.block = 256;
         return GEMM_OK;
     }
+    if (s.la != GEMM_LAYOUT_K_MAJOR || s.lb != GEMM_LAYOUT_K_MAJOR) return plan_layout(variant, s, cus, p);
     switch (variant) {
         case GEMM_VARIANT_SIMPLE: return plan_2d(s, K_SIMPLE_64, 64, p);
         case GEMM_VARIANT_MFMA: return plan_2d(s, K_MFMA_128, 128, p);
@@ -228,7 +266,8 @@ int make_plan(int variant, const Shape& s, int cus, Plan& p) {
 }
 
 int run(int variant, const Shape& s, void* stream) {
-    int rc = validate(s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC, s.out);
+    int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
+                      s.out);
     if (rc != GEMM_OK) return rc;
     if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_RING4) return GEMM_ERR_ARG;
     if (s.batch == 0 || s.M == 0 || s.N == 0) return GEMM_OK;
@@ -241,7 +280,7 @@ int run(int variant, const Shape& s, void* stream) {
     GemmArgs g{s.batch, s.M, s.N, s.K,
                static_cast<const uint16_t*>(s.A), s.lda, s.sA,
                static_cast<const uint16_t*>(s.B), s.ldb, s.sB,
-               const_cast<void*>(s.C), s.ldc, s.sC};
+               const_cast<void*>(s.C), s.ldc, s.sC, s.la, s.lb};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     switch (p.kernel) {
@@ -265,8 +304,23 @@ int run(int variant, const Shape& s, void* stream) {
 }
 
 Shape shape(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t sA,
-            const void* B, int64_t ldb, int64_t sB, const void* C, int64_t ldc, int64_t sC, int out) {
-    return Shape{batch, M, N, K, lda, sA, ldb, sB, ldc, sC, A, B, C, out};
+            const void* B, int64_t ldb, int64_t sB, const void* C, int64_t ldc, int64_t sC, int out,
+            int la = GEMM_LAYOUT_K_MAJOR, int lb = GEMM_LAYOUT_K_MAJOR) {
+    return Shape{batch, M, N, K, lda, sA, ldb, sB, ldc, sC, A, B, C, out, la, lb};
+}
+
+int plan_into(int variant, const Shape& s, int num_cus, int* kernel_id, int64_t* grid_x, int* block) {
+    int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
+                      s.out);
+    if (rc != GEMM_OK) return rc;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_RING4) return GEMM_ERR_ARG;
+    Plan p;
+    rc = make_plan(variant, s, num_cus > 0 ? num_cus : kDefaultCUs, p);
+    if (rc != GEMM_OK) return rc;
+    if (kernel_id) *kernel_id = p.kernel;
+    if (grid_x) *grid_x = int64_t(p.grid_x) * (p.grid_y ? p.grid_y : 1) * (p.grid_z ? p.grid_z : 1);
+    if (block) *block = p.block;
+    return GEMM_OK;
 }
 
 }  // namespace
@@ -296,23 +350,41 @@ int gemm_bf16_variant(int variant, int64_t batch, int64_t M, int64_t N, int64_t 
 int gemm_bf16_validate(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                        int64_t strideA, const void* B, int64_t ldb, int64_t strideB, const void* C,
                        int64_t ldc, int64_t strideC, int out_dtype) {
-    return validate(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype);
+    return validate(GEMM_LAYOUT_K_MAJOR, GEMM_LAYOUT_K_MAJOR, batch, M, N, K, A, lda, strideA, B, ldb, strideB,
+                    C, ldc, strideC, out_dtype);
 }
 
 int gemm_bf16_plan(int variant, int64_t batch, int64_t M, int64_t N, int64_t K, const void* A,
                    int64_t lda, int64_t strideA, const void* B, int64_t ldb, int64_t strideB,
                    const void* C, int64_t ldc, int64_t strideC, int out_dtype, int num_cus,
                    int* kernel_id, int64_t* grid_x, int* block) {
-    int rc = validate(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype);
-    if (rc != GEMM_OK) return rc;
-    Plan p;
-    rc = make_plan(variant, shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype),
-                   num_cus > 0 ? num_cus : kDefaultCUs, p);
-    if (rc != GEMM_OK) return rc;
-    if (kernel_id) *kernel_id = p.kernel;
-    if (grid_x) *grid_x = int64_t(p.grid_x) * (p.grid_y ? p.grid_y : 1) * (p.grid_z ? p.grid_z : 1);
-    if (block) *block = p.block;
-    return GEMM_OK;
+    return plan_into(variant, shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype),
+                     num_cus, kernel_id, grid_x, block);
+}
+
+int gemm_bf16_layout(int a_layout, int b_layout, int variant, int64_t batch, int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb, int64_t strideB,
+                     void* C, int64_t ldc, int64_t strideC, int out_dtype, void* stream) {
+    return run(variant,
+               shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype, a_layout, b_layout),
+               stream);
+}
+
+int gemm_bf16_layout_validate(int a_layout, int b_layout, int64_t batch, int64_t M, int64_t N, int64_t K,
+                              const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb,
+                              int64_t strideB, const void* C, int64_t ldc, int64_t strideC, int out_dtype) {
+    return validate(a_layout, b_layout, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                    out_dtype);
+}
+
+int gemm_bf16_layout_plan(int a_layout, int b_layout, int variant, int64_t batch, int64_t M, int64_t N,
+                          int64_t K, const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb,
+                          int64_t strideB, const void* C, int64_t ldc, int64_t strideC, int out_dtype,
+                          int num_cus, int* kernel_id, int64_t* grid_x, int* block) {
+    return plan_into(variant,
+                     shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype, a_layout,
+                           b_layout),
+                     num_cus, kernel_id, grid_x, block);
 }
 
 const char* gemm_bf16_kernel_name(int k) {

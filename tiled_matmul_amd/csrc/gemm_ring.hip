@@ -57,13 +57,25 @@ __device__ __forceinline__ int swz(int r) { return r & 7; }
 
 // MF: MFMA shape (16: v_mfma_f32_16x16x32_bf16, one per 32-deep k step and accumulator;
 // 32: v_mfma_f32_32x32x16_bf16, two per k step).
-template <int OUT, bool RAGGED, int WAVES_M, int WAVES_N, bool ASM, int MF>
+// MF: MFMA shape (16: v_mfma_f32_16x16x32_bf16, one per 32-deep k step and accumulator;
+// 32: v_mfma_f32_32x32x16_bf16, two per k step).  AMN / BMN: the A / B operand is MN-major
+// (element (i, k) at k * ld + i; MF = 16 only).  An MN-major tile sits in LDS as 64 k-rows
+// of 256 elements (512 bytes), 16-byte chunk c of k-row r at chunk c ^ 2 sigma(r) with
+// sigma(r) = (r ^ (r >> 2)) mod 8; its fragments are read with ds_read_b64_tr_b16, which
+// within each group of 16 lanes returns to lane i, element e, element (i mod 4) of the
+// 8 bytes addressed by lane 4 e + i / 4 (measured on MI355X).  So lane j of group g
+// addresses k-row 8 g + 4 e2 + j / 4, columns 4 (j mod 4) .. + 3 of the fragment, and lane
+// i receives the 4 consecutive k of column i: two such reads (e2 = 0, 1) make the MFMA
+// operand.  Each transpose read of 64 lanes touches 16 k-rows; sigma spreads them over 8
+// positions of a 256-byte bank row.
+template <int OUT, bool RAGGED, int WAVES_M, int WAVES_N, bool ASM, int MF, bool AMN, bool BMN>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void gemm_ring_kernel(
     GemmArgs g, TileGrid tg, int vec_store) {
     using namespace rg;
     using MM = std::conditional_t<MF == 16, std::conditional_t<ASM, MmaAsm16, Mma<16>>,
                                   std::conditional_t<ASM, MmaAsm32, Mma<32>>>;
     using Acc = typename MM::Acc;
+    static_assert(MF == 16 || !(AMN || BMN), "MN-major operands take the 16x16x32 shape");
     constexpr int KH = 32 / MM::KS;             // MFMAs per accumulator per 32-deep k step
     constexpr int CPM = MM::KS / 8;             // 16-byte k chunks per MFMA operand row
     constexpr int NW = WAVES_M * WAVES_N;
@@ -72,6 +84,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     constexpr int RTAIL = NW == 4 ? TMM_RING4_TAIL : TMM_RING8_TAIL;
     constexpr int L = 256 / (NW * R);   // load instructions per wave for one A (or B) tile
     static_assert(L * NW * R == 256, "rows split over the waves");
+    static_assert(64 / (NW * 2) == L, "an MN-major tile takes as many loads as a K-major one");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[(NA + NB) * TILE];
 
     const int lane = lane_id(), w = wave_id();
@@ -80,9 +93,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     const uint32_t K8 = RAGGED ? K & ~7u : K;
     const int nk = static_cast<int>((g.K + BK - 1) / BK);
 
-    // Load i of wave w: tile rows (NW i + w) R + lane / 8; the lane writes physical chunk
-    // lane % 8, i.e. fetches logical chunk (lane % 8) ^ swz(row).  R = 8, so swz(row) =
-    // lane / 8 for every i.
+    // K-major tiles.  Load i of wave w: tile rows (NW i + w) R + lane / 8; the lane writes
+    // physical chunk lane % 8, i.e. fetches logical chunk (lane % 8) ^ swz(row).  R = 8, so
+    // swz(row) = lane / 8 for every i.
     const int lrow = lane / 8;
     const uint32_t chunk_k = 8u * static_cast<uint32_t>((lane % 8) ^ swz(lrow));
     // Fragment reads of sub-step h of k step kk: row lane % MF of an MF-row block, logical
@@ -95,30 +108,93 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
             rd[kk][h] = (lane % MF) * ROWB + (((4 * kk + CPM * h + lane / MF) ^ swz(lane % MF)) * 16);
     const int a_off = wm * WM * ROWB, b_off = wn * WN * ROWB;
 
+    // MN-major tiles.  Load i of wave w: k-rows (NW i + w) 2 + lane / 32, physical chunk
+    // lane % 32, logical chunk (lane % 32) ^ 2 sigma(k-row).
+    auto sigma = [](int r) { return (r ^ (r >> 2)) & 7; };
+    int mn_col[L];   // element column (within the tile) this lane fetches in load i
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int r = (NW * i + w) * 2 + (lane >> 5);
+        mn_col[i] = 8 * ((lane & 31) ^ (2 * sigma(r)));
+    }
+    // Transpose reads: lane j of group gq addresses k-row 8 gq + 4 e2 + j / 4 (+ 32 kk) and
+    // columns col0 + 16 i + 4 (j mod 4); with col0 a multiple of 128 the physical chunk is
+    // col0 / 8 + 2 (i ^ sigma) + (j / 2) mod 2.
+    const int gq = lane >> 4, jl = lane & 15;
+    int tr_base[2], tr_sig[2];
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+        const int r = 8 * gq + 4 * e2 + (jl >> 2);
+        tr_sig[e2] = sigma(r);
+        tr_base[e2] = r * 512 + ((jl >> 1) & 1) * 16 + (jl & 1) * 8;
+    }
+    const int a_col0 = wm * WM, b_col0 = wn * WN;   // first fragment column of this wave
+
     for (int t = blockIdx.x; t < tg.total; t += gridDim.x) {
         int bt, tm, tn;
         tile_of(t, tg, bt, tm, tn);
         const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
         const int64_t rows_a = min<int64_t>(BM, g.M - m0), rows_b = min<int64_t>(BN, g.N - n0);
-        const uint16_t* Ab = g.A + bt * g.sA + m0 * g.lda;
-        const uint16_t* Bb = g.B + bt * g.sB + n0 * g.ldb;
-        const auto ra = make_rsrc(Ab, static_cast<uint32_t>(((rows_a - 1) * g.lda + g.K) * 2));
-        const auto rb = make_rsrc(Bb, static_cast<uint32_t>(((rows_b - 1) * g.ldb + g.K) * 2));
+        const uint16_t* Ab = g.A + bt * g.sA + (AMN ? m0 : m0 * g.lda);
+        const uint16_t* Bb = g.B + bt * g.sB + (BMN ? n0 : n0 * g.ldb);
+        const auto ra = make_rsrc(Ab, static_cast<uint32_t>(AMN ? ((g.K - 1) * g.lda + rows_a) * 2
+                                                                : ((rows_a - 1) * g.lda + g.K) * 2));
+        const auto rb = make_rsrc(Bb, static_cast<uint32_t>(BMN ? ((g.K - 1) * g.ldb + rows_b) * 2
+                                                                : ((rows_b - 1) * g.ldb + g.K) * 2));
+        // Per-lane offsets of each load (out-of-range rows or columns: OOB).
         uint32_t va[L], vb[L];
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            const int r = (NW * i + w) * R + lrow;
-            va[i] = r < rows_a ? static_cast<uint32_t>(r * g.lda) * 2u + 2u * chunk_k : OOB;
-            vb[i] = r < rows_b ? static_cast<uint32_t>(r * g.ldb) * 2u + 2u * chunk_k : OOB;
+            if constexpr (AMN) {
+                const int r = (NW * i + w) * 2 + (lane >> 5);
+                va[i] = mn_col[i] < rows_a ? static_cast<uint32_t>(r * g.lda + mn_col[i]) * 2u : OOB;
+            } else {
+                const int r = (NW * i + w) * R + lrow;
+                va[i] = r < rows_a ? static_cast<uint32_t>(r * g.lda) * 2u + 2u * chunk_k : OOB;
+            }
+            if constexpr (BMN) {
+                const int r = (NW * i + w) * 2 + (lane >> 5);
+                vb[i] = mn_col[i] < rows_b ? static_cast<uint32_t>(r * g.ldb + mn_col[i]) * 2u : OOB;
+            } else {
+                const int r = (NW * i + w) * R + lrow;
+                vb[i] = r < rows_b ? static_cast<uint32_t>(r * g.ldb) * 2u + 2u * chunk_k : OOB;
+            }
         }
 
-        // Load instruction q of the A (IS_A) or B tile of block j into the tile at LDS byte
-        // offset `dst` (chunks at k >= K8 read zeros; blocks past the end read zeros).
+        // Load instruction q of the A (is_a) or B tile of block j into the tile at LDS byte
+        // offset `dst` (k >= K8 reads zeros; blocks past the end read zeros).
         auto load_one = [&](bool is_a, int q, int j, int dst) {
             const uint32_t k0 = static_cast<uint32_t>(j) * BK;
-            const bool ok = k0 + chunk_k < K8;
-            load_lds_16(is_a ? ra : rb, lds + dst + (NW * q + w) * R * ROWB, ok ? (is_a ? va[q] : vb[q]) : OOB,
-                        2u * k0);
+            const bool mn = is_a ? AMN : BMN;
+            if (mn) {
+                const int64_t ld = is_a ? g.lda : g.ldb;
+                const uint32_t kr = static_cast<uint32_t>((NW * q + w) * 2 + (lane >> 5));
+                const bool ok = k0 + kr < K8;
+                // Blocks past the end get no row offset, so OOB + soffset cannot wrap into range.
+                const uint32_t soff = k0 < K ? static_cast<uint32_t>(k0 * ld) * 2u : 0u;
+                load_lds_16(is_a ? ra : rb, lds + dst + (NW * q + w) * 2 * 512, ok ? (is_a ? va[q] : vb[q]) : OOB,
+                            soff);
+            } else {
+                const bool ok = k0 + chunk_k < K8;
+                load_lds_16(is_a ? ra : rb, lds + dst + (NW * q + w) * R * ROWB, ok ? (is_a ? va[q] : vb[q]) : OOB,
+                            2u * k0);
+            }
+        };
+        // MN-major fragment i (16 columns from col0 + 16 i) of k step kk of the tile at `tile`.
+        // The transpose reads are inline assembly: issued through the builtin, LLVM waits for
+        // every outstanding direct-to-LDS load before each of them (it cannot tell that they
+        // read other slots).  Their completion is covered by the explicit lgkmcnt(0) that
+        // ends every k step (fenced by sched_barrier) before the fragments are used.
+        auto read_tr = [&](int tile, int col0, int i, int kk) {
+            u32x2 h[2];
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                const int off = tile + kk * 32 * 512 + tr_base[e2] + (col0 / 8) * 16 + 32 * (i ^ tr_sig[e2]);
+                const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(lds + off)));
+                asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(h[e2]) : "v"(addr) : "memory");
+            }
+            const u32x4 v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3);
+            return __builtin_bit_cast(bf16x8, v);
         };
         // Fragment q of k step kk from the A tile at `at` and the B tile at `bt_`: q < KH FN:
         // B fragment q % FN of sub-step q / FN, else A fragment (q - KH FN) % FM of sub-step
@@ -127,10 +203,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         auto read_one = [&](F& f, int q, int at, int bt_, int kk) {
             if (q < KH * FN) {
                 const int h = q / FN, i = q % FN;
-                f.b[q] = *reinterpret_cast<const bf16x8*>(lds + bt_ + b_off + MF * i * ROWB + rd[kk][h]);
+                if constexpr (BMN)
+                    f.b[q] = read_tr(bt_, b_col0, i, kk);
+                else
+                    f.b[q] = *reinterpret_cast<const bf16x8*>(lds + bt_ + b_off + MF * i * ROWB + rd[kk][h]);
             } else {
                 const int r = q - KH * FN, h = r / FM, j = r % FM;
-                f.a[r] = *reinterpret_cast<const bf16x8*>(lds + at + a_off + MF * j * ROWB + rd[kk][h]);
+                if constexpr (AMN)
+                    f.a[r] = read_tr(at, a_col0, j, kk);
+                else
+                    f.a[r] = *reinterpret_cast<const bf16x8*>(lds + at + a_off + MF * j * ROWB + rd[kk][h]);
             }
         };
         constexpr int NR = KH * (FN + FM);
@@ -181,25 +263,44 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
 
         if constexpr (RAGGED) {
             // Elements K8 .. K - 1 of every row, element by element (nothing at or beyond K is
-            // read), as chunk 0 of one more 32-deep step (A in A slot 0, B in B slot 0);
-            // chunks 1-3 are zero.
-            for (int r = threadIdx.x; r < BM + BN; r += 64 * NW) {
-                const bool is_a = r < BM;
-                const int rr = is_a ? r : r - BM;
-                uint32_t hv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (rr < (is_a ? rows_a : rows_b)) {
-                    const uint16_t* row = is_a ? Ab + rr * g.lda : Bb + rr * g.ldb;
+            // read), as the first 8 k of one more 32-deep step (A in A slot 0, B in B slot 0),
+            // each tile in its own layout; the rest of the step is zero.
+            auto stage = [&](bool is_a, bool mn, const uint16_t* Xb, int64_t ld, int64_t rows, int dst) {
+                if (mn) {
+                    // k-rows 0 .. 31 of the MN-major tile; row e < 8 holds k = K8 + e.
+                    for (int c = threadIdx.x; c < 32 * 32; c += 64 * NW) {
+                        const int r = c >> 5, lc = c & 31, col = 8 * lc;
+                        uint32_t hv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                        if (r < 8 && K8 + r < K) {
 #pragma unroll
-                    for (int e = 0; e < 7; ++e)
-                        if (K8 + e < K) hv[e] = row[K8 + e];
+                            for (int e = 0; e < 8; ++e)
+                                if (col + e < rows) hv[e] = Xb[(K8 + r) * ld + col + e];
+                        }
+                        const u32x4 v = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                                         hv[6] | (hv[7] << 16)};
+                        *reinterpret_cast<u32x4*>(lds + dst + r * 512 + ((lc ^ (2 * sigma(r))) * 16)) = v;
+                    }
+                } else {
+                    for (int rr = threadIdx.x; rr < 256; rr += 64 * NW) {
+                        uint32_t hv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                        if (rr < rows) {
+                            const uint16_t* row = Xb + rr * ld;
+#pragma unroll
+                            for (int e = 0; e < 7; ++e)
+                                if (K8 + e < K) hv[e] = row[K8 + e];
+                        }
+                        uint8_t* d = lds + dst + rr * ROWB;
+                        const u32x4 z = {0u, 0u, 0u, 0u};
+                        const u32x4 v = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                                         hv[6] | (hv[7] << 16)};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(d + ((c ^ swz(rr)) * 16)) = c == 0 ? v : z;
+                    }
                 }
-                uint8_t* dst = lds + (is_a ? 0 : B_BASE) + rr * ROWB;
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                const u32x4 v = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
-                                 hv[6] | (hv[7] << 16)};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(dst + ((c ^ swz(rr)) * 16)) = c == 0 ? v : z;
-            }
+                (void)is_a;
+            };
+            stage(true, AMN, Ab, g.lda, rows_a, 0);
+            stage(false, BMN, Bb, g.ldb, rows_b, B_BASE);
             barrier();
 #pragma unroll
             for (int q = 0; q < NR; ++q) read_one(f[0], q, 0, B_BASE, 0);
@@ -223,19 +324,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     }
 }
 
-template <int WM, int WN, bool ASM, int MF>
-static hipError_t launch_ring_cfg(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
+template <int WM, int WN, bool ASM, int MF, bool AMN, bool BMN>
+static hipError_t launch_ring_lay(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
     const bool ragged = (g.K & 7) != 0;
     const dim3 grid(p.grid_x), block(64 * WM * WN);
     if (out == OUT_F32 && ragged)
-        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, true, WM, WN, ASM, MF>), grid, block, 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, true, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g, p.grid,
+                           p.vec_store);
     else if (out == OUT_F32)
-        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, false, WM, WN, ASM, MF>), grid, block, 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, false, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g, p.grid,
+                           p.vec_store);
     else if (ragged)
-        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, true, WM, WN, ASM, MF>), grid, block, 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, true, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g, p.grid,
+                           p.vec_store);
     else
-        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, false, WM, WN, ASM, MF>), grid, block, 0, s, g, p.grid, p.vec_store);
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, false, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g, p.grid,
+                           p.vec_store);
     return hipGetLastError();
+}
+
+// K-major operands: any ring configuration; MN-major ones: the 4-wave, 16x16x32 kernel.
+template <int WM, int WN, bool ASM, int MF>
+static hipError_t launch_ring_cfg(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
+    if (g.la == LAYOUT_K && g.lb == LAYOUT_K) return launch_ring_lay<WM, WN, ASM, MF, false, false>(g, out, p, s);
+    if constexpr (WM == 2 && WN == 2) {
+        if (g.la == LAYOUT_K) return launch_ring_lay<2, 2, true, 16, false, true>(g, out, p, s);
+        if (g.lb == LAYOUT_K) return launch_ring_lay<2, 2, true, 16, true, false>(g, out, p, s);
+        return launch_ring_lay<2, 2, true, 16, true, true>(g, out, p, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 // MFMA shape of the ring kernels (16 or 32; v_mfma_f32_32x32x16_bf16 measured 5-7% slower on

@@ -1,7 +1,8 @@
 // The first rungs of the GEMM ladder, C = A * B^T with A (M x K) and B (N x K) bf16,
 // K-contiguous, fp32 accumulation.  Both kernels load through plain per-lane global loads,
 // handle any pitch and alignment (2-byte aligned operands), and mask every tail, so they
-// also serve as the general fallback of the fast kernels.
+// also serve as the general fallback of the fast kernels; gemm_simple_kernel also takes
+// MN-major operands (the general fallback for those layouts).
 //
 //   gemm_simple_kernel  -- the page "读书笔记-《面向机器学习系统的现代 GPU 编程》", section
 //                          "9 步优化", steps 1-3: one workgroup per 64 x 64 output tile of
@@ -50,13 +51,23 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(GemmArgs g) {
     const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
     float acc[4][4] = {};
     for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
+        // Consecutive threads walk the contiguous direction of each operand: k for a
+        // K-major operand, m (n) for an MN-major one.
 #pragma unroll
         for (int i = 0; i < (T * BK) / 256; ++i) {
-            const int e = tid + 256 * i, r = e / BK, kk = e % BK;
-            const int64_t gk = k0 + kk;
-            const int64_t gm = m0 + r, gn = n0 + r;
-            As[kk][r] = (gm < g.M && gk < g.K) ? bf16_to_f32(A[gm * g.lda + gk]) : 0.0f;
-            Bs[kk][r] = (gn < g.N && gk < g.K) ? bf16_to_f32(B[gn * g.ldb + gk]) : 0.0f;
+            const int e = tid + 256 * i;
+            {
+                const int r = g.la == LAYOUT_K ? e / BK : e % T, kk = g.la == LAYOUT_K ? e % BK : e / T;
+                const int64_t gk = k0 + kk, gm = m0 + r;
+                const int64_t off = g.la == LAYOUT_K ? gm * g.lda + gk : gk * g.lda + gm;
+                As[kk][r] = (gm < g.M && gk < g.K) ? bf16_to_f32(A[off]) : 0.0f;
+            }
+            {
+                const int r = g.lb == LAYOUT_K ? e / BK : e % T, kk = g.lb == LAYOUT_K ? e % BK : e / T;
+                const int64_t gk = k0 + kk, gn = n0 + r;
+                const int64_t off = g.lb == LAYOUT_K ? gn * g.ldb + gk : gk * g.ldb + gn;
+                Bs[kk][r] = (gn < g.N && gk < g.K) ? bf16_to_f32(B[off]) : 0.0f;
+            }
         }
         __syncthreads();
 #pragma unroll 8

@@ -85,14 +85,16 @@ __device__ __forceinline__ void step(Acc (&acc)[FN][FM], const F& f, RD rd, LD l
         constexpr int KH = static_cast<int>(sizeof(f.b) / sizeof(f.b[0])) / FN;
         constexpr int NMK = NM * KH;
         static_assert(TAIL < NMK, "reads need MFMAs to hide behind");
+        constexpr int D = NMK - TAIL;
 #pragma unroll
         for (int m = 0; m < NMK; ++m) {
+            // reads q with q D / NR == m, loads q with q NMK / NG == m
+            const int r0 = m < D ? (m * NR + D - 1) / D : NR, r1 = m < D ? ((m + 1) * NR + D - 1) / D : NR;
+            const int g0 = (m * NG + NMK - 1) / NMK, g1 = ((m + 1) * NG + NMK - 1) / NMK;
 #pragma unroll
-            for (int q = 0; q < NR; ++q)
-                if (q * (NMK - TAIL) / NR == m) rd(q);
+            for (int q = r0; q < (r1 < NR ? r1 : NR); ++q) rd(q);
 #pragma unroll
-            for (int q = 0; q < NG; ++q)
-                if (q * NMK / NG == m) ld(q);
+            for (int q = g0; q < (g1 < NG ? g1 : NG); ++q) ld(q);
             __builtin_amdgcn_sched_barrier(0);
             const int h = m / NM, i = (m % NM) / FM, j = m % FM;
             acc[i][j] = M::run(f.b[h * FN + i], f.a[h * FM + j], acc[i][j]);
