@@ -130,15 +130,33 @@ def gemm_leg(args, torch):
     log(f"[bench] generating {name} operands")
     (A, B), sets = make_sets(name, torch, args.rotate_mb * 2 ** 20, la, lb)
     variant = tm.VARIANTS[args.variant]
-    rc, kname, grid, block = tm.gemm_bf16_layout_plan(
-        la, lb, variant, batch, M, N, K, sets[0][0], lda, sA, sets[0][1], ldb, sB, sets[0][2], N,
-        sC, out, torch.cuda.get_device_properties(0).multi_processor_count)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    splits = None
+    if args.splits is not None:
+        # split K: plan with an unbounded workspace, then allocate what the plan needs
+        rc, splits, kname, grid = tm.gemm_bf16_splitk_plan(
+            la, lb, args.splits, batch, M, N, K, sets[0][0], lda, sA, sets[0][1], ldb, sB,
+            sets[0][2], N, sC, out, 1 << 12, 1 << 62, cus)
+        block = 256
+        ws_bytes = splits * batch * M * N * 4
+        ws = torch.empty(max(ws_bytes // 4, 4), dtype=torch.float32, device="cuda")
+        if splits > 1:
+            kname += "+splitk_reduce"
+    else:
+        rc, kname, grid, block = tm.gemm_bf16_layout_plan(
+            la, lb, variant, batch, M, N, K, sets[0][0], lda, sA, sets[0][1], ldb, sB, sets[0][2],
+            N, sC, out, cus)
     if rc != 0:
         raise SystemExit(f"variant {args.variant} cannot run {name}: {tm.gemm_bf16_status_string(rc)}")
 
     def launch(i):
         a, b, c = sets[i]
-        tm.gemm_bf16_layout(la, lb, variant, batch, M, N, K, a, lda, sA, b, ldb, sB, c, N, sC, out)
+        if splits is not None:
+            tm.gemm_bf16_splitk(la, lb, args.splits, batch, M, N, K, a, lda, sA, b, ldb, sB, c, N,
+                                sC, out, ws, ws_bytes)
+        else:
+            tm.gemm_bf16_layout(la, lb, variant, batch, M, N, K, a, lda, sA, b, ldb, sB, c, N,
+                                sC, out)
 
     log(f"[bench] timing {name}: kernel {kname}, {len(sets)} rotating buffer sets, "
         f"{args.warmup} warm-up + {args.steps} timed steps")
@@ -152,6 +170,7 @@ def gemm_leg(args, torch):
         "layouts": f"A {args.a_layout}-major, B {args.b_layout}-major",
         "out": "fp32" if out == 0 else "bf16",
         "kernel": kname, "grid": grid, "block": block, "ms": ms, "wall_s": wall,
+        "splits": splits,
         "tflops": tflops, "flops": flops, "bytes": nbytes, "A": A, "B": B, "sets": sets,
     }
 
@@ -288,6 +307,9 @@ def main():
                     help="A stored M x K (k) or K x M (mn)")
     ap.add_argument("--b-layout", default="k", choices=["k", "mn"],
                     help="B stored N x K (k) or K x N (mn: C = A B)")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="run the GEMM through gemm_bf16_splitk with this many K ranges "
+                         "(0: the library's choice)")
     ap.add_argument("--rotate-mb", type=int, default=512,
                     help="total size of the rotating input/output sets")
     ap.add_argument("--gemv-workload", default="gemv_m1", choices=["gemv_m1", "gemv_m16"],
@@ -333,7 +355,7 @@ def main():
                                + f"M={res['M']} N={res['N']} K={res['K']}, bf16 in, "
                                f"fp32 accumulate, {res['out']} out",
                    "layouts": res["layouts"], "variant": args.variant, "kernel": res["kernel"],
-                   "grid": res["grid"], "block": res["block"],
+                   "grid": res["grid"], "block": res["block"], "splits": res["splits"],
                    "rotating_buffer_sets": len(res["sets"])},
         "pct_mfma_peak": 100.0 * res["tflops"] / MFMA_TFLOPS,
         "roofline": gemm_roofline(res),

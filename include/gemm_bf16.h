@@ -185,6 +185,57 @@ int gemm_bf16_layout_plan(int a_layout, int b_layout, int variant, int64_t batch
                           int out_dtype, int num_cus,
                           int* kernel_id, int64_t* grid_x, int* block);
 
+/*
+ * Split K (for problems with too few output tiles to fill the device, but a long K).  The
+ * page "读书笔记-《面向机器学习系统的现代 GPU 编程》", section "9 步优化", builds the
+ * output of one tile as the sum over the K blocks of their partial products (step 2) and
+ * hands tiles to a fixed pool of persistent workgroups (step 6).  Here a work item of that
+ * pool is (tile, K range): the K blocks of 64 are cut into `S` contiguous ranges; each work
+ * item writes its range's fp32 partial sum to the workspace, and a second kernel adds the S
+ * partials of each element in range order (0, 1, ..., S-1) and rounds once to out_dtype.
+ * The result is deterministic (the same bits on every run with the same S) and differs from
+ * gemm_bf16_layout only in the order of the fp32 additions.
+ *   splits           S >= 1 to force (capped at the number of K blocks, ceil(K / 64)), or 0
+ *                    to let the library choose: S = 1 when the 256 x 256 tiles already
+ *                    fill 90 % of the compute units, else the most ranges that fill them
+ *                    (at least 4 K blocks per range) and fit in the workspace.
+ *   workspace        device memory owned by the caller, 16-byte aligned, at least
+ *                    S * batch * M * N * 4 bytes (see gemm_bf16_splitk_plan for S); only
+ *                    used, and may be NULL, when S == 1.  Its contents on entry do not
+ *                    matter; it is scratch until the call's work on `stream` completes, so
+ *                    calls that share a workspace must be ordered on one stream.
+ *   workspace_bytes  its size in bytes.
+ * Other arguments as gemm_bf16_layout (every layout).  When S == 1 the call is exactly
+ * gemm_bf16_layout(a_layout, b_layout, GEMM_VARIANT_AUTO, ...).  When S > 1 it runs the
+ * 4-wave ring kernel, which needs what that kernel needs with the layouts given (4-byte
+ * aligned A and B, even pitches and strides; an MN-major extent a multiple of 8): if these
+ * do not hold, an explicit splits > 1 returns GEMM_ERR_UNSUPPORTED and splits == 0 falls
+ * back to S = 1.  A workspace that is too small or misaligned returns GEMM_ERR_ARG (NULL:
+ * GEMM_ERR_NULL); splits < 0 or workspace_bytes < 0: GEMM_ERR_ARG.  Nothing is launched on
+ * an error.
+ */
+int gemm_bf16_splitk(int a_layout, int b_layout, int splits, int64_t batch,
+                     int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda, int64_t strideA,
+                     const void* B, int64_t ldb, int64_t strideB,
+                     void* C, int64_t ldc, int64_t strideC,
+                     int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Host-only plan of gemm_bf16_splitk on a device with `num_cus` compute units (0: 256):
+ * *splits_out receives S, *kernel_id the kernel of the first launch and *grid_x its
+ * workgroups.  To size a workspace, pass workspace_bytes = INT64_MAX with a non-NULL
+ * 16-byte aligned workspace pointer and allocate S * batch * M * N * 4 bytes.  Returns the
+ * status gemm_bf16_splitk would return before launching.  Output pointers may be NULL.
+ */
+int gemm_bf16_splitk_plan(int a_layout, int b_layout, int splits, int64_t batch,
+                          int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t lda, int64_t strideA,
+                          const void* B, int64_t ldb, int64_t strideB,
+                          const void* C, int64_t ldc, int64_t strideC,
+                          int out_dtype, const void* workspace, int64_t workspace_bytes,
+                          int num_cus, int* splits_out, int* kernel_id, int64_t* grid_x);
+
 /* Name of a kernel id from gemm_bf16_plan ("?" if unknown).  Static storage. */
 const char* gemm_bf16_kernel_name(int kernel_id);
 

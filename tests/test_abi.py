@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tm.gemm_bf16_version() == 4
+    assert tm.gemm_bf16_version() == 5
     for s in range(7):
         assert tm.gemm_bf16_status_string(s).startswith("GEMM_")
     assert tm.gemm_bf16_status_string(99) == "unknown status"
@@ -189,3 +189,55 @@ def test_layout_plan():
     assert lplan(MN, MN, K=0, lda=4096, ldb=4096)[:2] == (0, "zero_fill")
     # both K-major: the K-major planner (the GEMV path included)
     assert lplan(KM, KM, M=1)[:2] == (0, "gemv_lds")
+
+
+def splan(splits, M=1024, N=1024, K=16384, la=0, lb=0, ws=P, ws_bytes=(1 << 62), out=0,
+          batch=1, lda=None, ldb=None, A=P, B=P):
+    lda = (K if la == 0 else M) if lda is None else lda
+    ldb = (K if lb == 0 else N) if ldb is None else ldb
+    sA, sB, sC = (M * K, N * K, M * N) if batch > 1 else (0, 0, 0)
+    return tm.gemm_bf16_splitk_plan(la, lb, splits, batch, M, N, K, A, lda, sA, B, ldb, sB, P, N,
+                                    sC, out, ws, ws_bytes, 256)
+
+
+def test_splitk_plan():
+    MN, KM = tm.GEMM_LAYOUT_MN_MAJOR, tm.GEMM_LAYOUT_K_MAJOR
+    # unsplit, the planner would run 64 tiles of 128 x 128 (a quarter of the CUs busy); split,
+    # 16 tiles of 256 x 256 times 16 K ranges (of 16 blocks of 64) fill the 256 CUs
+    assert splan(0) == (0, 16, "ring4_256", 256)
+    # the workspace bounds the choice: room for 5 ranges
+    assert splan(0, ws_bytes=5 * 1024 * 1024 * 4 + 100)[:2] == (0, 5)
+    # no workspace: one range, the ordinary AUTO plan
+    assert splan(0, ws=None, ws_bytes=0)[:3] == (0, 1, "persist_128")
+    # at least 8 K blocks per range: K = 1024 (16 blocks) -> 2 ranges
+    assert splan(0, K=1024)[:2] == (0, 2)
+    assert splan(0, K=960)[:3] == (0, 1, "persist_128")
+    # enough tiles already (4096^2: 256 tiles; 64 items of 256 x 256: 256 tiles of 128 x 128):
+    # one range
+    assert splan(0, M=4096, N=4096, K=4096) == (0, 1, "ring4_256", 256)
+    assert splan(0, M=256, N=256, K=1024, batch=64)[:3] == (0, 1, "persist_128")
+    # explicit counts, capped at the number of K blocks
+    assert splan(3, M=4096, N=4096, K=4096) == (0, 3, "ring4_256", 256)
+    assert splan(7, K=128) == (0, 2, "ring4_256", 32)
+    assert splan(1)[:2] == (0, 1)
+    assert splan(7, K=128, ws=None, ws_bytes=0)[0] == tm.GEMM_ERR_NULL
+    # workspace checks: too small, misaligned, negative sizes and counts
+    assert splan(2, ws_bytes=2 * 1024 * 1024 * 4)[0] == 0
+    assert splan(2, ws_bytes=2 * 1024 * 1024 * 4 - 1)[0] == tm.GEMM_ERR_ARG
+    assert splan(2, ws=P + 4)[0] == tm.GEMM_ERR_ARG
+    assert splan(-1)[0] == tm.GEMM_ERR_ARG
+    assert splan(0, ws_bytes=-1)[0] == tm.GEMM_ERR_ARG
+    # layouts: MN-major operands split like K-major ones
+    assert splan(0, la=MN, lb=MN)[:3] == (0, 16, "ring4_256")
+    # the ring kernel cannot run (MN-major N not a multiple of 8): forced -> unsupported,
+    # automatic -> one range on the general kernel
+    assert splan(2, lb=MN, N=1020)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert splan(0, lb=MN, N=1020)[:3] == (0, 1, "simple_64")
+    # skinny M: the GEMV path, never split automatically
+    assert splan(0, M=1)[:3] == (0, 1, "gemv_lds")
+    assert splan(0, M=16)[:3] == (0, 1, "gemv")
+    # K = 0: zero fill, whatever the count
+    assert splan(0, K=0, lda=1, ldb=1)[:3] == (0, 1, "zero_fill")
+    assert splan(5, K=0, lda=1, ldb=1)[:3] == (0, 1, "zero_fill")
+    # bad arguments are reported as by the other entry points
+    assert splan(2, lda=100)[0] == tm.GEMM_ERR_ARG

@@ -86,9 +86,13 @@ def _load():
     lib.gemm_bf16_layout_validate.argtypes = [_int, _int] + batched
     lib.gemm_bf16_layout_plan.argtypes = [_int, _int, _int] + batched + [
         _int, ctypes.POINTER(_int), ctypes.POINTER(_i64), ctypes.POINTER(_int)]
+    lib.gemm_bf16_splitk.argtypes = [_int, _int, _int] + batched + [_vp, _i64, _vp]
+    lib.gemm_bf16_splitk_plan.argtypes = [_int, _int, _int] + batched + [
+        _vp, _i64, _int, ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_i64)]
     for f in ("gemm_bf16", "gemm_bf16_strided_batched", "gemm_bf16_variant",
               "gemm_bf16_validate", "gemm_bf16_plan", "gemm_bf16_version", "gemm_bf16_layout",
-              "gemm_bf16_layout_validate", "gemm_bf16_layout_plan"):
+              "gemm_bf16_layout_validate", "gemm_bf16_layout_plan", "gemm_bf16_splitk",
+              "gemm_bf16_splitk_plan"):
         getattr(lib, f).restype = _int
     lib.gemm_bf16_kernel_name.argtypes = [_int]
     lib.gemm_bf16_kernel_name.restype = ctypes.c_char_p
@@ -195,6 +199,27 @@ def gemm_bf16_layout_plan(a_layout, b_layout, variant, batch, M, N, K, A, lda, s
                                        out_dtype, num_cus, ctypes.byref(k), ctypes.byref(g),
                                        ctypes.byref(b))
     return rc, gemm_bf16_kernel_name(k.value), g.value, b.value
+
+
+def gemm_bf16_splitk(a_layout, b_layout, splits, batch, M, N, K, A, lda, strideA, B, ldb,
+                     strideB, C, ldc, strideC, out_dtype, workspace, workspace_bytes,
+                     stream=None):
+    _check(_load().gemm_bf16_splitk(a_layout, b_layout, splits, batch, M, N, K, _ptr(A), lda,
+                                    strideA, _ptr(B), ldb, strideB, _ptr(C), ldc, strideC,
+                                    out_dtype, _ptr(workspace), workspace_bytes,
+                                    _stream(stream)), "gemm_bf16_splitk")
+
+
+def gemm_bf16_splitk_plan(a_layout, b_layout, splits, batch, M, N, K, A, lda, strideA, B, ldb,
+                          strideB, C, ldc, strideC, out_dtype, workspace, workspace_bytes,
+                          num_cus=0):
+    """(status, splits, kernel_name, workgroups of the first launch)."""
+    s, k, g = _int(0), _int(0), _i64(0)
+    rc = _load().gemm_bf16_splitk_plan(a_layout, b_layout, splits, batch, M, N, K, _ptr(A), lda,
+                                       strideA, _ptr(B), ldb, strideB, _ptr(C), ldc, strideC,
+                                       out_dtype, _ptr(workspace), workspace_bytes, num_cus,
+                                       ctypes.byref(s), ctypes.byref(k), ctypes.byref(g))
+    return rc, s.value, gemm_bf16_kernel_name(k.value), g.value
 
 
 def gemm_bf16_kernel_name(kernel_id: int) -> str:

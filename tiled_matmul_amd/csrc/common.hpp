@@ -28,6 +28,11 @@ struct GemmArgs {
     void* C;
     int64_t ldc, sC;
     int la = LAYOUT_K, lb = LAYOUT_K;
+    // Split K: each tile's K blocks are divided into `splits` contiguous ranges; with
+    // splits > 1 each range's fp32 partial product goes to ws[s][batch][M][N] and a reduction
+    // writes C.
+    float* ws = nullptr;
+    int splits = 1;
 };
 
 // Tile grid of one launch: tiles_m x tiles_n tiles per batch item, `total` over the batch.

@@ -11,7 +11,7 @@ using namespace tmm;
 
 namespace {
 
-constexpr int kVersion = 4;
+constexpr int kVersion = 5;
 constexpr int kDefaultCUs = 256;        // MI355X
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t k2G = int64_t(1) << 31;
@@ -303,6 +303,79 @@ int run(int variant, const Shape& s, void* stream) {
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// --- split K --------------------------------------------------------------------------
+// Number of K ranges for gemm_bf16_splitk: `splits` if > 0 (capped at the K blocks of 64),
+// else (auto, `auto_tiles` = tiles of the kernel the planner would run without splitting):
+// one range when those tiles keep at least half the CUs busy, else the most ranges of at
+// least 8 K blocks that fill the CUs with 256 x 256 tiles and fit in the workspace.
+int choose_splits(const Shape& s, int splits, int64_t ws_bytes, int cus, int64_t auto_tiles) {
+    const int64_t nk = cdiv(s.K, 64);
+    const int64_t per = s.batch * s.M * s.N * 4;   // workspace bytes per range
+    const int64_t tiles = cdiv(s.M, 256) * cdiv(s.N, 256) * s.batch;
+    int64_t S;
+    if (splits > 0) {
+        S = std::min<int64_t>(splits, nk);
+    } else {
+        if (auto_tiles * 2 > cus) return 1;
+        S = std::min<int64_t>(cus / tiles, nk / 8);
+        S = std::min<int64_t>(S, ws_bytes / per);
+    }
+    S = std::min<int64_t>(S, 256);
+    if (tiles * S >= k2G) S = k2G / tiles - 1;
+    return static_cast<int>(std::max<int64_t>(S, 1));
+}
+
+// Plan of gemm_bf16_splitk: *S = ranges (1: an ordinary gemm_bf16_layout call with AUTO).
+int plan_splitk(const Shape& s, int splits, const void* ws, int64_t ws_bytes, int cus, int* S, Plan& p) {
+    if (splits < 0 || ws_bytes < 0) return GEMM_ERR_ARG;
+    *S = 1;
+    if (s.batch == 0 || s.M == 0 || s.N == 0 || s.K == 0) return make_plan(GEMM_VARIANT_AUTO, s, cus, p);
+    int64_t auto_tiles = 0;
+    if (splits == 0) {   // only where the library would run a tiled MFMA kernel anyway
+        int rc = make_plan(GEMM_VARIANT_AUTO, s, cus, p);
+        if (rc != GEMM_OK) return rc;
+        if (p.kernel != K_RING4_256 && p.kernel != K_PERSIST_128 && p.kernel != K_PERSIST_256) return GEMM_OK;
+        auto_tiles = p.grid.total;
+    }
+    const int want = choose_splits(s, splits, ws_bytes, cus, auto_tiles);
+    if (want > 1 && !ring_layout_ok(s)) {   // the ring kernel's own preconditions
+        if (splits > 1) return GEMM_ERR_UNSUPPORTED;
+        return make_plan(GEMM_VARIANT_AUTO, s, cus, p);
+    }
+    if (want <= 1) return make_plan(GEMM_VARIANT_AUTO, s, cus, p);
+    if (ws == nullptr) return GEMM_ERR_NULL;
+    if (!aligned(ws, 16) || ws_bytes < int64_t(want) * s.batch * s.M * s.N * 4) return GEMM_ERR_ARG;
+    int rc = plan_spec(s, cus, p, K_RING4_256);
+    if (rc != GEMM_OK) return rc;
+    p.grid_x = static_cast<int>(std::min<int64_t>(int64_t(p.grid.total) * want, cus));
+    *S = want;
+    return GEMM_OK;
+}
+
+int run_splitk(const Shape& s, int splits, void* ws, int64_t ws_bytes, void* stream) {
+    int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
+                      s.out);
+    if (rc != GEMM_OK) return rc;
+    if (s.batch == 0 || s.M == 0 || s.N == 0) return GEMM_OK;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != GEMM_OK) return rc;
+    Plan p;
+    int S = 1;
+    rc = plan_splitk(s, splits, ws, ws_bytes, cus, &S, p);
+    if (rc != GEMM_OK) return rc;
+    if (S == 1) return run(GEMM_VARIANT_AUTO, s, stream);
+    GemmArgs g{s.batch, s.M, s.N, s.K,
+               static_cast<const uint16_t*>(s.A), s.lda, s.sA,
+               static_cast<const uint16_t*>(s.B), s.ldb, s.sB,
+               const_cast<void*>(s.C), s.ldc, s.sC, s.la, s.lb,
+               static_cast<float*>(ws), S};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_ring(g, s.out, p, st);
+    if (e == hipSuccess) e = launch_splitk_reduce(g, s.out, st);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 Shape shape(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t sA,
             const void* B, int64_t ldb, int64_t sB, const void* C, int64_t ldc, int64_t sC, int out,
             int la = GEMM_LAYOUT_K_MAJOR, int lb = GEMM_LAYOUT_K_MAJOR) {
@@ -385,6 +458,35 @@ int gemm_bf16_layout_plan(int a_layout, int b_layout, int variant, int64_t batch
                      shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype, a_layout,
                            b_layout),
                      num_cus, kernel_id, grid_x, block);
+}
+
+int gemm_bf16_splitk(int a_layout, int b_layout, int splits, int64_t batch, int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb, int64_t strideB,
+                     void* C, int64_t ldc, int64_t strideC, int out_dtype, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+    return run_splitk(
+        shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype, a_layout, b_layout),
+        splits, workspace, workspace_bytes, stream);
+}
+
+int gemm_bf16_splitk_plan(int a_layout, int b_layout, int splits, int64_t batch, int64_t M, int64_t N,
+                          int64_t K, const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb,
+                          int64_t strideB, const void* C, int64_t ldc, int64_t strideC, int out_dtype,
+                          const void* workspace, int64_t workspace_bytes, int num_cus, int* splits_out,
+                          int* kernel_id, int64_t* grid_x) {
+    const Shape s =
+        shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype, a_layout, b_layout);
+    int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
+                      s.out);
+    if (rc != GEMM_OK) return rc;
+    Plan p;
+    int S = 1;
+    rc = plan_splitk(s, splits, workspace, workspace_bytes, num_cus > 0 ? num_cus : kDefaultCUs, &S, p);
+    if (rc != GEMM_OK) return rc;
+    if (splits_out) *splits_out = S;
+    if (kernel_id) *kernel_id = p.kernel;
+    if (grid_x) *grid_x = int64_t(p.grid_x) * (p.grid_y ? p.grid_y : 1) * (p.grid_z ? p.grid_z : 1);
+    return GEMM_OK;
 }
 
 const char* gemm_bf16_kernel_name(int k) {

@@ -30,6 +30,8 @@
 //
 // Preconditions (planner): A, B 4-byte aligned with even pitches and strides, 256 * ld * 2
 // below 2^31.  A ragged K tail (K mod 8 != 0) is staged through LDS as one extra k step.
+#include <algorithm>
+
 #include "launch.hpp"
 #include "mfma_step.hpp"
 
@@ -68,6 +70,11 @@ __device__ __forceinline__ int swz(int r) { return r & 7; }
 // i receives the 4 consecutive k of column i: two such reads (e2 = 0, 1) make the MFMA
 // operand.  Each transpose read of 64 lanes touches 16 k-rows; sigma spreads them over 8
 // positions of a 256-byte bank row.
+// OUT: OUT_F32 or OUT_BF16 into C, or OUT_PARTIAL: split K, the fp32 partial sum of each work
+// item's K range into the workspace (its own instance, so that the other instances keep one
+// range per tile as a compile-time constant and their registers).
+constexpr int OUT_PARTIAL = 2;
+
 template <int OUT, bool RAGGED, int WAVES_M, int WAVES_N, bool ASM, int MF, bool AMN, bool BMN>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void gemm_ring_kernel(
     GemmArgs g, TileGrid tg, int vec_store) {
@@ -91,7 +98,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     const int wm = w / WAVES_N, wn = w % WAVES_N;
     const uint32_t K = static_cast<uint32_t>(g.K);
     const uint32_t K8 = RAGGED ? K & ~7u : K;
-    const int nk = static_cast<int>((g.K + BK - 1) / BK);
+    const int nk_all = static_cast<int>((g.K + BK - 1) / BK);
+    const int S = OUT == OUT_PARTIAL ? g.splits : 1;   // K ranges per tile
 
     // K-major tiles.  Load i of wave w: tile rows (NW i + w) R + lane / 8; the lane writes
     // physical chunk lane % 8, i.e. fetches logical chunk (lane % 8) ^ swz(row).  R = 8, so
@@ -130,7 +138,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     }
     const int a_col0 = wm * WM, b_col0 = wn * WN;   // first fragment column of this wave
 
-    for (int t = blockIdx.x; t < tg.total; t += gridDim.x) {
+    for (int item = blockIdx.x; item < tg.total * S; item += gridDim.x) {
+        // Work item = (tile, K range); range s covers blocks [s nk / S, (s + 1) nk / S).
+        const int t = item / S, s_rng = item - (item / S) * S;
+        const int kb0 = static_cast<int>(static_cast<int64_t>(s_rng) * nk_all / S);
+        const int nk = static_cast<int>(static_cast<int64_t>(s_rng + 1) * nk_all / S) - kb0;
         int bt, tm, tn;
         tile_of(t, tg, bt, tm, tn);
         const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
@@ -163,8 +175,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
 
         // Load instruction q of the A (is_a) or B tile of block j into the tile at LDS byte
         // offset `dst` (k >= K8 reads zeros; blocks past the end read zeros).
+        // Blocks j >= nk of this range are loaded too (the last iterations run ahead); they
+        // are never read, whatever they hold.
         auto load_one = [&](bool is_a, int q, int j, int dst) {
-            const uint32_t k0 = static_cast<uint32_t>(j) * BK;
+            const uint32_t k0 = static_cast<uint32_t>(kb0 + j) * BK;
             const bool mn = is_a ? AMN : BMN;
             if (mn) {
                 const int64_t ld = is_a ? g.lda : g.ldb;
@@ -261,7 +275,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         wait_vmcnt<0>();   // the trailing zero-fill loads have landed
         barrier();         // every fragment read of this tile is done: the rings are free
 
-        if constexpr (RAGGED) {
+        if (RAGGED && s_rng == S - 1) {   // the last range holds the end of K (uniform branch)
             // Elements K8 .. K - 1 of every row, element by element (nothing at or beyond K is
             // read), as the first 8 k of one more 32-deep step (A in A slot 0, B in B slot 0),
             // each tile in its own layout; the rest of the step is zero.
@@ -315,20 +329,116 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         }
         if constexpr (ASM) agpr_fence(acc);
 
-        void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
-                                  : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
-        if constexpr (MF == 16)
-            store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
-        else
-            store_acc32<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
+        if constexpr (OUT == OUT_PARTIAL) {   // range s_rng's partial (pitch N; 16-byte stores when N % 4 == 0)
+            float* P = g.ws + (static_cast<int64_t>(s_rng) * g.batch + bt) * g.M * g.N;
+            if constexpr (MF == 16)
+                store_acc<OUT_F32, FN, FM>(P, g.N, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, g.N % 4 == 0);
+            else
+                store_acc32<OUT_F32, FN, FM>(P, g.N, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, g.N % 4 == 0);
+        } else {
+            void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
+                                      : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
+            if constexpr (MF == 16)
+                store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
+            else
+                store_acc32<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
+        }
     }
+}
+
+// Split-K reduction: C[b][m][n] = sum over s = 0 .. S-1, in that order, of ws[s][b][m][n]
+// (fp32 sums; deterministic), converted to the output type.  V = 4: four consecutive
+// elements of one row per thread (N % 4 == 0), 16-byte workspace loads, the S loads of a
+// thread issued before they are summed; VC: C takes 16-byte (fp32) or 8-byte (bf16) stores.
+template <int OUT, int V, bool VC>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
+    const int64_t mn = g.M * g.N, total = g.batch * mn, nv = total / V;
+    for (int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; v < nv;
+         v += static_cast<int64_t>(gridDim.x) * 256) {
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = 0.f;
+        constexpr int U = 8;   // loads in flight per thread
+        for (int s0 = 0; s0 < g.splits; s0 += U) {
+            float x[U][V];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (s0 + u < g.splits) {
+                    const float* src = g.ws + (s0 + u) * total + v * V;
+                    if constexpr (V == 4) {
+                        const f32x4 t = *reinterpret_cast<const f32x4*>(src);
+                        x[u][0] = t[0], x[u][1] = t[1], x[u][2] = t[2], x[u][3] = t[3];
+                    } else {
+                        x[u][0] = *src;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (s0 + u < g.splits)
+#pragma unroll
+                    for (int i = 0; i < V; ++i) acc[i] += x[u][i];
+        }
+        const int64_t e = v * V, b = e / mn, r = e - b * mn, m = r / g.N, n = r - m * g.N;
+        const int64_t off = b * g.sC + m * g.ldc + n;
+        if constexpr (OUT == OUT_F32) {
+            float* c = static_cast<float*>(g.C) + off;
+            if constexpr (VC) {
+                *reinterpret_cast<f32x4*>(c) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; ++i) c[i] = acc[i];
+            }
+        } else {
+            uint16_t* c = static_cast<uint16_t*>(g.C) + off;
+            if constexpr (VC) {
+                const uint32_t lo = f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+                const uint32_t hi = f32_to_bf16(acc[2]) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+                *reinterpret_cast<u32x2*>(c) = u32x2{lo, hi};
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; ++i) c[i] = f32_to_bf16(acc[i]);
+            }
+        }
+    }
+}
+
+template <int OUT>
+static void launch_reduce_out(const GemmArgs& g, bool v4, bool vc, int blocks, hipStream_t s) {
+    if (v4 && vc)
+        hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 4, true>), dim3(blocks), dim3(256), 0, s, g);
+    else if (v4)
+        hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 4, false>), dim3(blocks), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 1, false>), dim3(blocks), dim3(256), 0, s, g);
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs& g, int out, hipStream_t s) {
+    const int64_t total = g.batch * g.M * g.N;
+    const bool v4 = g.N % 4 == 0;   // the workspace is 16-byte aligned with pitch N
+    const uintptr_t ca = out == OUT_F32 ? 16 : 8;
+    const bool vc = v4 && reinterpret_cast<uintptr_t>(g.C) % ca == 0 && g.ldc % 4 == 0 &&
+                    (g.batch == 1 || g.sC % 4 == 0);
+    const int64_t threads = v4 ? total / 4 : total;
+    const int blocks = static_cast<int>(std::min<int64_t>((threads + 255) / 256, 65536));
+    if (out == OUT_F32)
+        launch_reduce_out<OUT_F32>(g, v4, vc, blocks, s);
+    else
+        launch_reduce_out<OUT_BF16>(g, v4, vc, blocks, s);
+    return hipGetLastError();
 }
 
 template <int WM, int WN, bool ASM, int MF, bool AMN, bool BMN>
 static hipError_t launch_ring_lay(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
     const bool ragged = (g.K & 7) != 0;
     const dim3 grid(p.grid_x), block(64 * WM * WN);
-    if (out == OUT_F32 && ragged)
+    if (g.splits > 1 && ragged)
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_PARTIAL, true, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g,
+                           p.grid, p.vec_store);
+    else if (g.splits > 1)
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_PARTIAL, false, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g,
+                           p.grid, p.vec_store);
+    else if (out == OUT_F32 && ragged)
         hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, true, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g, p.grid,
                            p.vec_store);
     else if (out == OUT_F32)

@@ -42,6 +42,7 @@ hipError_t launch_mfma(const GemmArgs& g, int out, const Plan& p, hipStream_t s)
 hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_pingpong(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_ring(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_splitk_reduce(const GemmArgs& g, int out, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_gemv_lds(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 int gemv_lds_rows_per_workgroup();

@@ -191,6 +191,11 @@ WORKLOADS = {
     "batched_64x256x256x1024": dict(cfg=5, M=256, N=256, K=1024, batch=64,
                                     a=("uniform", (-1.0, 1.0)), b=("uniform", (-1.0, 1.0)),
                                     out=OUT_FP32),
+    # Not one of the five: the FFN down projection for a batch of 256 tokens (few output
+    # tiles, long K), the shape split K is for.  The FFN configuration's distributions.
+    "ffn_down_256x4096x14336": dict(cfg=4, M=256, N=4096, K=14336, batch=1,
+                                    a=("normal", (1.0,)), b=("normal", (0.02,)),
+                                    out=OUT_BF16),
 }
 
 
