@@ -107,15 +107,18 @@ def time_steps(launch, nsets, steps, warmup, torch):
 
 def traffic_for(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return t.get("hbm_bytes_per_launch")
+    the current kernel sources; else None.  "a+b" (a call of two kernels) sums both."""
+    total = 0
+    for part in kernel.split("+"):
+        path = os.path.join(ROOT, "profiles", f"traffic_{part}_{workload}.json")
+        if not os.path.exists(path):
+            return None
+        with open(path) as f:
+            t = json.load(f)
+        if t.get("kernel_source_sha") != kernel_source_sha():
+            return None
+        total += t.get("hbm_bytes_per_launch")
+    return total
 
 
 def gemm_leg(args, torch):
