@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tm.gemm_bf16_version() == 5
+    assert tm.gemm_bf16_version() == 6
     for s in range(7):
         assert tm.gemm_bf16_status_string(s).startswith("GEMM_")
     assert tm.gemm_bf16_status_string(99) == "unknown status"
@@ -241,3 +241,43 @@ def test_splitk_plan():
     assert splan(5, K=0, lda=1, ldb=1)[:3] == (0, 1, "zero_fill")
     # bad arguments are reported as by the other entry points
     assert splan(2, lda=100)[0] == tm.GEMM_ERR_ARG
+
+
+def mxplan(variant=0, fa=0, fb=0, M=4096, N=4096, K=4096, A=P, lda=None, SA=P, ldsa=None, B=P,
+           ldb=None, SB=P, ldsb=None, out=0):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldsa = max(K // 32, 1) if ldsa is None else ldsa
+    ldsb = max(K // 32, 1) if ldsb is None else ldsb
+    return tm.gemm_mx_plan(variant, fa, fb, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, P, N, out,
+                           256)
+
+
+def test_mx_validation_and_plan():
+    assert mxplan()[:2] == (0, "mx_ring_256") and mxplan()[2:] == (256, 256)
+    assert mxplan(fa=1, fb=0, out=1)[:2] == (0, "mx_ring_256")
+    # K not a multiple of 128, odd pitches, unaligned operands or scales: general kernel
+    assert mxplan(K=4064)[:2] == (0, "mx_simple_64")
+    assert mxplan(lda=4098)[:2] == (0, "mx_simple_64")
+    assert mxplan(ldsa=130)[:2] == (0, "mx_simple_64")
+    assert mxplan(A=P + 2)[:2] == (0, "mx_simple_64")
+    assert mxplan(SB=P + 1)[:2] == (0, "mx_simple_64")
+    assert mxplan(M=100, N=70, K=4064)[2] == 2 * 2
+    # forced kernels
+    assert mxplan(variant=1)[:2] == (0, "mx_simple_64")
+    assert mxplan(variant=2, K=4064)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert mxplan(variant=3)[0] == tm.GEMM_ERR_ARG
+    # argument errors
+    assert mxplan(K=4016)[0] == tm.GEMM_ERR_ARG          # K % 32
+    assert mxplan(fa=2)[0] == tm.GEMM_ERR_ARG
+    assert mxplan(lda=4095)[0] == tm.GEMM_ERR_ARG
+    assert mxplan(ldsa=127)[0] == tm.GEMM_ERR_ARG
+    assert mxplan(out=2)[0] == tm.GEMM_ERR_DTYPE
+    assert mxplan(SA=None)[0] == tm.GEMM_ERR_NULL
+    assert mxplan(M=-1)[0] == tm.GEMM_ERR_ARG
+    # empty products
+    assert mxplan(K=0, lda=1, ldb=1)[:2] == (0, "zero_fill")
+    assert mxplan(M=0)[:2] == (0, "none")
+    v = tm.gemm_mx_validate
+    assert v(0, 0, 64, 64, 64, P, 64, P, 2, P, 64, P, 2, P, 64, 0) == tm.GEMM_OK
+    assert v(0, 0, 64, 64, 64, P, 64, P, 1, P, 64, P, 2, P, 64, 0) == tm.GEMM_ERR_ARG

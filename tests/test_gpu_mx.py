@@ -1,0 +1,157 @@
+"""GPU parity of the block-scaled 8-bit GEMM (gemm_mx, gemm_mx_variant) against the CPU
+oracle (oracle/mx.py).
+
+Integer-valued elements (|v| <= 4) with scales within a factor 2 of 1 keep every product,
+every group sum of the scaled MFMA and every fp32 partial sum exact, so there both kernels
+must equal the oracle bitwise (fp32 out) or its round-to-nearest-even bf16 (bf16 out).
+Quantised normal values are checked against the block-scaled bound (check_mx).  Padding
+bytes hold NaN codes and NaN scales: a kernel that reads them fails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import check as ck
+from oracle import mx
+import tiled_matmul_amd as tm
+from tiled_matmul_amd import synth
+
+from helpers import OUT_BF16, OUT_FP32, empty_out, out_to_host
+
+pytestmark = pytest.mark.gpu
+
+AUTO, SIMPLE, RING = tm.GEMM_MX_VARIANT_AUTO, tm.GEMM_MX_VARIANT_SIMPLE, tm.GEMM_MX_VARIANT_RING
+PAIRS = [(0, 0), (1, 1), (0, 1), (1, 0)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+
+
+def dev(x: np.ndarray, offset: int = 0):
+    """uint8 array -> device uint8 tensor view starting ``offset`` bytes into a buffer."""
+    import torch
+    flat = np.ascontiguousarray(x).reshape(-1)
+    buf = torch.zeros(flat.size + offset + 64, dtype=torch.uint8, device="cuda")
+    buf[offset:offset + flat.size].copy_(torch.from_numpy(flat))
+    return buf[offset:offset + flat.size]
+
+
+def run_mx(A, SA, B, SB, fa, fb, K, out_dtype, variant=AUTO, a_off=0, b_off=0, s_off=0):
+    """One gemm_mx_variant call; A (M x lda), SA (M x lds) etc. are host arrays."""
+    M, N = A.shape[0], B.shape[0]
+    C = empty_out(M, N, out_dtype, fill=7)
+    Ag, SAg = dev(A, a_off), dev(SA, s_off)
+    Bg, SBg = dev(B, b_off), dev(SB, s_off)
+    tm.gemm_mx_variant(variant, fa, fb, M, N, K, Ag, A.shape[1], SAg, SA.shape[1], Bg,
+                       B.shape[1], SBg, SB.shape[1], C, N, out_dtype)
+    return out_to_host(C, M, N, N, out_dtype)
+
+
+def plan(A, SA, B, SB, fa, fb, K, variant=AUTO, a_off=0, s_off=0):
+    P = 1 << 12
+    return tm.gemm_mx_plan(variant, fa, fb, A.shape[0], B.shape[0], K, P + a_off, A.shape[1],
+                           P + s_off, SA.shape[1], P, B.shape[1], P + s_off, SB.shape[1], P,
+                           B.shape[0], 0)[1]
+
+
+def expect_exact(got, A, SA, B, SB, fa, fb, K, out_dtype, rows=None, what=""):
+    C, _, _ = mx.gemm(A, SA, B, SB, fa, fb, K=K, rows=rows)
+    exp = C.astype(np.float32) if out_dtype == OUT_FP32 else oracle.round_bf16(C)
+    r = ck.check_exact(got, exp, out_dtype)
+    assert r["ok"], f"{what}: {r}"
+
+
+# (M, N, K): K % 128 == 0 takes the scaled-MFMA ring kernel; the others the general kernel.
+SHAPES = [(256, 256, 128), (264, 136, 1024), (520, 264, 384), (64, 1000, 256), (136, 72, 128),
+          (300, 200, 4096), (200, 130, 96), (33, 65, 32), (256, 256, 160)]
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_mx_integer_exact(fa, fb, M, N, K):
+    A, SA = synth.mx_integers(M, K, 701 + M + K, fa)
+    B, SB = synth.mx_integers(N, K, 702 + N + K, fb)
+    variants = [AUTO, SIMPLE] + ([RING] if K % 128 == 0 else [])
+    assert plan(A, SA, B, SB, fa, fb, K) == ("mx_ring_256" if K % 128 == 0 else "mx_simple_64")
+    for variant in variants:
+        for out_dtype in (OUT_FP32, OUT_BF16):
+            got = run_mx(A, SA, B, SB, fa, fb, K, out_dtype, variant)
+            expect_exact(got, A, SA, B, SB, fa, fb, K, out_dtype,
+                         what=f"{M}x{N}x{K} formats {fa}{fb} variant {variant} out {out_dtype}")
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("variant", [AUTO, SIMPLE])
+def test_mx_quantised_normals_within_bound(fa, fb, variant):
+    M, N, K = 520, 392, 2048
+    A, SA = synth.mx_operand("normal", M, K, 711, fa, (1.0,))
+    B, SB = synth.mx_operand("normal", N, K, 712, fb, (0.02,))
+    C, Mag, F = mx.gemm(A, SA, B, SB, fa, fb)
+    for out_dtype in (OUT_FP32, OUT_BF16):
+        got = run_mx(A, SA, B, SB, fa, fb, K, out_dtype, variant)
+        r = ck.check_mx(got, C, Mag, F, K, out_dtype)
+        assert r["ok"], r
+
+
+def test_mx_padded_pitches_and_offsets():
+    """Pitches beyond the extents (NaN padding), 4-byte offsets (ring kernel) and 1-byte
+    offsets (general kernel)."""
+    M, N, K = 264, 136, 512
+    A, SA = synth.mx_integers(M, K, 721, 0, ld=K + 4, lds=K // 32 + 4)
+    B, SB = synth.mx_integers(N, K, 722, 1, ld=K + 12, lds=K // 32 + 8)
+    assert plan(A, SA, B, SB, 0, 1, K, a_off=4, s_off=4) == "mx_ring_256"
+    assert plan(A, SA, B, SB, 0, 1, K, a_off=1) == "mx_simple_64"
+    for a_off, s_off in ((0, 0), (4, 4), (1, 3)):
+        got = run_mx(A, SA, B, SB, 0, 1, K, OUT_FP32, a_off=a_off, b_off=a_off, s_off=s_off)
+        expect_exact(got, A, SA, B, SB, 0, 1, K, OUT_FP32, what=f"offsets {a_off} {s_off}")
+
+
+def test_mx_k_zero_and_errors():
+    import torch
+    C = empty_out(40, 48, OUT_FP32, fill=3)
+    dummy = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    tm.gemm_mx(0, 0, 40, 48, 0, dummy, 1, dummy, 1, dummy, 1, dummy, 1, C, 48, OUT_FP32)
+    assert np.all(out_to_host(C, 40, 48, 48, OUT_FP32) == 0)
+    A, SA = synth.mx_integers(64, 96, 731, 0)
+    with pytest.raises(tm.GemmError) as e:   # K not a multiple of 32
+        run_mx(A, SA, A, SA, 0, 0, 80, OUT_FP32)
+    assert e.value.status == tm.GEMM_ERR_ARG
+    with pytest.raises(tm.GemmError) as e:   # the ring kernel needs K % 128 == 0
+        run_mx(A, SA, A, SA, 0, 0, 96, OUT_FP32, variant=RING)
+    assert e.value.status == tm.GEMM_ERR_UNSUPPORTED
+    with pytest.raises(tm.GemmError) as e:
+        run_mx(A, SA, A, SA, 2, 0, 96, OUT_FP32)
+    assert e.value.status == tm.GEMM_ERR_ARG
+
+
+def test_mx_deterministic():
+    M, N, K = 512, 512, 1024
+    A, SA = synth.mx_operand("normal", M, K, 741, 0, (1.0,))
+    B, SB = synth.mx_operand("normal", N, K, 742, 0, (1.0,))
+    g1 = run_mx(A, SA, B, SB, 0, 0, K, OUT_FP32)
+    g2 = run_mx(A, SA, B, SB, 0, 0, K, OUT_FP32)
+    assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", sorted(synth.MX_WORKLOADS))
+def test_mx_workloads_full_size_sampled(name):
+    """Every MX workload at full size: sampled rows of C against the oracle (bound), and the
+    same shape with integer values (bitwise)."""
+    w = synth.MX_WORKLOADS[name]
+    M, N, K, fa, fb, out = w["M"], w["N"], w["K"], w["fa"], w["fb"], w["out"]
+    rows = sorted({0, 1, 255, 256, M - 1} | set(np.random.default_rng(9).integers(0, M, 6).tolist()))
+    A, SA, B, SB = synth.make_mx_operands(name)
+    got = run_mx(A, SA, B, SB, fa, fb, K, out)
+    C, Mag, F = mx.gemm(A, SA, B, SB, fa, fb, rows=rows)
+    r = ck.check_mx(got[rows], C, Mag, F, K, out)
+    assert r["ok"], r
+    Ai, SAi = synth.mx_integers(M, K, 751, fa)
+    Bi, SBi = synth.mx_integers(N, K, 752, fb)
+    got = run_mx(Ai, SAi, Bi, SBi, fa, fb, K, out)
+    expect_exact(got[rows], Ai, SAi, Bi, SBi, fa, fb, K, out, rows=rows, what=name)

@@ -1,0 +1,148 @@
+"""Pins of the block-scaled 8-bit oracle (oracle/mx.py) to things other than itself: the
+format definitions (values fixed by the bit layout), PyTorch's own float8 conversions (an
+independent library routine), brute force with exactly rounded sums, the bf16 oracle on
+inputs both formats represent, and the effect of one block scale.  CPU only."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import check as ck
+from oracle import mx
+from tiled_matmul_amd import synth
+
+torch = pytest.importorskip("torch")
+
+ALL = np.arange(256, dtype=np.uint8)
+
+
+@pytest.mark.parametrize("fmt,dt", [(mx.E4M3, torch.float8_e4m3fn), (mx.E5M2, torch.float8_e5m2)])
+def test_decode_matches_torch_for_every_code(fmt, dt):
+    ours = mx.decode(ALL, fmt)
+    ref = torch.from_numpy(ALL.copy()).view(dt).to(torch.float64).numpy()
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert np.all(both_nan | (ours == ref)), np.nonzero(~(both_nan | (ours == ref)))
+    assert np.array_equal(np.signbit(ours[~both_nan]), np.signbit(ref[~both_nan]))
+
+
+def test_decode_values_fixed_by_the_formats():
+    e4 = lambda c: float(mx.decode(np.array([c], np.uint8), mx.E4M3)[0])
+    e5 = lambda c: float(mx.decode(np.array([c], np.uint8), mx.E5M2)[0])
+    assert e4(0x38) == 1.0 and e4(0xB8) == -1.0
+    assert e4(0x7E) == 448.0                      # largest finite E4M3
+    assert e4(0x08) == 2.0 ** -6                   # smallest normal
+    assert e4(0x01) == 2.0 ** -9                   # smallest subnormal
+    assert e4(0x07) == 7 * 2.0 ** -9
+    assert math.isnan(e4(0x7F)) and math.isnan(e4(0xFF))
+    assert e4(0x77) == 240.0 and e4(0x4C) == 6.0 and e4(0x46) == 3.5
+    assert e5(0x3C) == 1.0 and e5(0x7B) == 57344.0
+    assert e5(0x04) == 2.0 ** -14 and e5(0x01) == 2.0 ** -16
+    assert e5(0x7C) == math.inf and e5(0xFC) == -math.inf and math.isnan(e5(0x7D))
+
+
+def test_scale_and_exponent_field():
+    s = mx.decode_scale(np.array([0, 126, 127, 128, 254, 255], np.uint8))
+    assert list(s[:5]) == [2.0 ** -127, 0.5, 1.0, 2.0, 2.0 ** 127] and math.isnan(s[5])
+    f = mx.exponent_field(np.array([0x38, 0x01, 0x00, 0x7E, 0xC0], np.uint8), mx.E4M3)
+    assert list(f) == [0, -6, -6, 8, 1]
+    f = mx.exponent_field(np.array([0x3C, 0x01, 0x7B], np.uint8), mx.E5M2)
+    assert list(f) == [0, -14, 15]
+
+
+def brute(A, SA, B, SB, fa, fb, K):
+    """Pure-Python loops over the decoded table, exactly rounded sums (math.fsum)."""
+    tabA = {c: float(v) for c, v in zip(range(256), mx.decode(ALL, fa))}
+    tabB = {c: float(v) for c, v in zip(range(256), mx.decode(ALL, fb))}
+    M, N = A.shape[0], B.shape[0]
+    C = np.zeros((M, N))
+    for i in range(M):
+        for j in range(N):
+            C[i, j] = math.fsum(tabA[int(A[i, k])] * 2.0 ** (int(SA[i, k // 32]) - 127) *
+                                tabB[int(B[j, k])] * 2.0 ** (int(SB[j, k // 32]) - 127)
+                                for k in range(K))
+    return C
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 1), (0, 1), (1, 0)])
+def test_brute_force_tiny(fa, fb):
+    M, N, K = 3, 5, 96
+    A, SA = synth.mx_operand("normal", M, K, 11, fa, (1.0,))
+    B, SB = synth.mx_operand("normal", N, K, 12, fb, (0.5,))
+    C, Mag, F = mx.gemm(A, SA, B, SB, fa, fb)
+    Cb = brute(A, SA, B, SB, fa, fb, K)
+    assert C.shape == (M, N)
+    assert np.all(np.abs(C - Cb) <= 2.0 ** -50 * Mag)
+    assert np.all(F >= 0) and np.all(Mag <= 4.0 * F + 1e-300)   # |product| < 4 2^(ea+eb)
+
+
+def test_rows_subset():
+    A, SA = synth.mx_operand("normal", 9, 64, 21, 0, (1.0,))
+    B, SB = synth.mx_operand("normal", 4, 64, 22, 0, (1.0,))
+    C, Mag, F = mx.gemm(A, SA, B, SB, 0, 0)
+    Cr, Mr, Fr = mx.gemm(A, SA, B, SB, 0, 0, rows=[7, 2])
+    assert np.array_equal(Cr, C[[7, 2]]) and np.array_equal(Fr, F[[7, 2]])
+
+
+def test_block_scale_applies_to_its_32_columns_only():
+    """Raising one scale code by one doubles exactly that block's contribution to its row."""
+    M, N, K = 4, 3, 128
+    A, SA = synth.mx_integers(M, K, 31, mx.E4M3)
+    B, SB = synth.mx_integers(N, K, 32, mx.E4M3)
+    C, _, _ = mx.gemm(A, SA, B, SB, 0, 0)
+    i, q = 2, 1
+    SA2 = SA.copy()
+    SA2[i, q] += 1
+    C2, _, _ = mx.gemm(A, SA2, B, SB, 0, 0)
+    contrib = brute(A[:, q * 32:(q + 1) * 32], SA[:, q:q + 1], B[:, q * 32:(q + 1) * 32],
+                    SB[:, q:q + 1], 0, 0, 32)
+    assert np.array_equal(C2[i] - C[i], contrib[i])
+    assert np.array_equal(np.delete(C2, i, 0), np.delete(C, i, 0))
+
+
+@pytest.mark.parametrize("fmt", [mx.E4M3, mx.E5M2])
+def test_unit_scales_reduce_to_the_bf16_oracle(fmt):
+    """With every scale 1 (code 127) the MX GEMM is the bf16 GEMM of the decoded elements
+    (both 8-bit formats are exact in bf16); integer values keep both sums exact."""
+    M, N, K = 6, 7, 160
+    A, SA = synth.mx_integers(M, K, 41, fmt, scale_lo=127, scale_hi=127)
+    B, SB = synth.mx_integers(N, K, 42, fmt, scale_lo=127, scale_hi=127)
+    C, _, _ = mx.gemm(A, SA, B, SB, fmt, fmt)
+    Ab = oracle.round_bf16(mx.decode(A, fmt))
+    Bb = oracle.round_bf16(mx.decode(B, fmt))
+    Cb, _ = oracle.gemm(Ab, Bb)
+    assert np.array_equal(C, Cb)
+
+
+def test_identity_closed_form():
+    """A = I (ones on the diagonal, scale 1) => C = B's scaled values transposed."""
+    K = 64
+    A = np.zeros((K, K), np.uint8)
+    A[np.arange(K), np.arange(K)] = 0x38
+    SA = np.full((K, 2), 127, np.uint8)
+    B, SB = synth.mx_operand("normal", 5, K, 51, mx.E5M2, (1.0,))
+    C, _, _ = mx.gemm(A, SA, B, SB, mx.E4M3, mx.E5M2)
+    assert np.array_equal(C, mx.scaled(B, SB, mx.E5M2, K).T)
+
+
+def test_quantiser_roundtrip_error():
+    """The generator's quantisation keeps values within the formats' relative precision of
+    the drawn normals (a check of the input recipe, not of the GEMM)."""
+    A, SA = synth.mx_operand("normal", 8, 256, 61, mx.E4M3, (1.0,))
+    v = mx.scaled(A, SA, mx.E4M3, 256)
+    assert np.all(np.isfinite(v)) and np.abs(v).max() < 8
+    assert np.all(SA[:, :8] <= 127 - 8 + 3) and np.all(SA[:, :8] >= 127 - 8 - 12)
+
+
+def test_check_mx_accepts_rounding_and_rejects_a_wrong_block():
+    M, N, K = 8, 8, 256
+    A, SA = synth.mx_operand("normal", M, K, 71, 0, (1.0,))
+    B, SB = synth.mx_operand("normal", N, K, 72, 0, (1.0,))
+    C, Mag, F = mx.gemm(A, SA, B, SB, 0, 0)
+    ok = ck.check_mx(C.astype(np.float32), C, Mag, F, K, ck.OUT_FP32)
+    assert ok["ok"]
+    SAw = SA.copy()
+    SAw[:, 3] = SAw[:, 3] + 1           # one block's scale wrong by a factor 2
+    Cw, _, _ = mx.gemm(A, SAw, B, SB, 0, 0)
+    bad = ck.check_mx(Cw.astype(np.float32), C, Mag, F, K, ck.OUT_FP32)
+    assert not bad["ok"]

@@ -20,6 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # tile-shape macros by tiled_matmul_amd.build.build_library(out=..., defines=...)).
 LIB_PATH = os.environ.get("GEMM_BF16_LIB") or os.path.join(_HERE, "libgemm_bf16.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gemm_bf16.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(_HERE), "include", "gemm_mx.h")]
 
 GEMM_OK = 0
 GEMM_ERR_ARG = 1
@@ -34,6 +35,13 @@ GEMM_OUT_BF16 = 1
 
 GEMM_LAYOUT_K_MAJOR = 0
 GEMM_LAYOUT_MN_MAJOR = 1
+
+# Block-scaled 8-bit GEMM (include/gemm_mx.h)
+GEMM_MX_E4M3 = 0
+GEMM_MX_E5M2 = 1
+GEMM_MX_VARIANT_AUTO = 0
+GEMM_MX_VARIANT_SIMPLE = 1
+GEMM_MX_VARIANT_RING = 2
 
 GEMM_VARIANT_AUTO = 0
 GEMM_VARIANT_SIMPLE = 1
@@ -89,6 +97,14 @@ def _load():
     lib.gemm_bf16_splitk.argtypes = [_int, _int, _int] + batched + [_vp, _i64, _vp]
     lib.gemm_bf16_splitk_plan.argtypes = [_int, _int, _int] + batched + [
         _vp, _i64, _int, ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_i64)]
+    mx = [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int]
+    lib.gemm_mx.argtypes = mx + [_vp]
+    lib.gemm_mx_variant.argtypes = [_int] + mx + [_vp]
+    lib.gemm_mx_validate.argtypes = mx
+    lib.gemm_mx_plan.argtypes = [_int] + mx + [_int, ctypes.POINTER(_int), ctypes.POINTER(_i64),
+                                                ctypes.POINTER(_int)]
+    for f in ("gemm_mx", "gemm_mx_variant", "gemm_mx_validate", "gemm_mx_plan"):
+        getattr(lib, f).restype = _int
     for f in ("gemm_bf16", "gemm_bf16_strided_batched", "gemm_bf16_variant",
               "gemm_bf16_validate", "gemm_bf16_plan", "gemm_bf16_version", "gemm_bf16_layout",
               "gemm_bf16_layout_validate", "gemm_bf16_layout_plan", "gemm_bf16_splitk",
@@ -108,10 +124,12 @@ def library():
 
 
 def declared_functions() -> list[str]:
-    """Names of the functions include/gemm_bf16.h declares."""
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gemm_bf16\w*)\s*\(", text, re.M)))
+    """Names of the functions include/gemm_bf16.h and include/gemm_mx.h declare."""
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gemm_\w*)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def _ptr(x):
@@ -220,6 +238,39 @@ def gemm_bf16_splitk_plan(a_layout, b_layout, splits, batch, M, N, K, A, lda, st
                                        out_dtype, _ptr(workspace), workspace_bytes, num_cus,
                                        ctypes.byref(s), ctypes.byref(k), ctypes.byref(g))
     return rc, s.value, gemm_bf16_kernel_name(k.value), g.value
+
+
+def gemm_mx(a_format, b_format, M, N, K, A, lda, A_scale, lda_scale, B, ldb, B_scale, ldb_scale, C,
+            ldc, out_dtype, stream=None):
+    _check(_load().gemm_mx(a_format, b_format, M, N, K, _ptr(A), lda, _ptr(A_scale), lda_scale,
+                           _ptr(B), ldb, _ptr(B_scale), ldb_scale, _ptr(C), ldc, out_dtype,
+                           _stream(stream)), "gemm_mx")
+
+
+def gemm_mx_variant(variant, a_format, b_format, M, N, K, A, lda, A_scale, lda_scale, B, ldb,
+                    B_scale, ldb_scale, C, ldc, out_dtype, stream=None):
+    _check(_load().gemm_mx_variant(variant, a_format, b_format, M, N, K, _ptr(A), lda,
+                                   _ptr(A_scale), lda_scale, _ptr(B), ldb, _ptr(B_scale),
+                                   ldb_scale, _ptr(C), ldc, out_dtype, _stream(stream)),
+           "gemm_mx_variant")
+
+
+def gemm_mx_validate(a_format, b_format, M, N, K, A, lda, A_scale, lda_scale, B, ldb, B_scale,
+                     ldb_scale, C, ldc, out_dtype) -> int:
+    return _load().gemm_mx_validate(a_format, b_format, M, N, K, _ptr(A), lda, _ptr(A_scale),
+                                    lda_scale, _ptr(B), ldb, _ptr(B_scale), ldb_scale, _ptr(C),
+                                    ldc, out_dtype)
+
+
+def gemm_mx_plan(variant, a_format, b_format, M, N, K, A, lda, A_scale, lda_scale, B, ldb,
+                 B_scale, ldb_scale, C, ldc, out_dtype, num_cus=0):
+    """(status, kernel_name, workgroups, threads_per_workgroup)."""
+    k, g, b = _int(0), _i64(0), _int(0)
+    rc = _load().gemm_mx_plan(variant, a_format, b_format, M, N, K, _ptr(A), lda, _ptr(A_scale),
+                              lda_scale, _ptr(B), ldb, _ptr(B_scale), ldb_scale, _ptr(C), ldc,
+                              out_dtype, num_cus, ctypes.byref(k), ctypes.byref(g),
+                              ctypes.byref(b))
+    return rc, gemm_bf16_kernel_name(k.value), g.value, b.value
 
 
 def gemm_bf16_kernel_name(kernel_id: int) -> str:

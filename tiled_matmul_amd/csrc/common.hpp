@@ -36,6 +36,24 @@ struct GemmArgs {
 };
 
 // Tile grid of one launch: tiles_m x tiles_n tiles per batch item, `total` over the batch.
+// Block-scaled 8-bit GEMM (gemm_mx): element formats (the codes the scaled MFMA takes) and
+// arguments; pitches and sizes in bytes, one E8M0 scale byte per 32 k of a row.
+enum { MX_E4M3 = 0, MX_E5M2 = 1 };
+struct MxArgs {
+    int64_t M, N, K;
+    const uint8_t* A;
+    int64_t lda;
+    const uint8_t* SA;
+    int64_t ldsa;
+    const uint8_t* B;
+    int64_t ldb;
+    const uint8_t* SB;
+    int64_t ldsb;
+    void* C;
+    int64_t ldc;
+    int fa, fb;
+};
+
 struct TileGrid {
     int tiles_m, tiles_n, total, group_m;
 };

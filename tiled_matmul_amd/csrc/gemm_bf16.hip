@@ -5,13 +5,14 @@
 #include <string.h>
 
 #include "gemm_bf16.h"
+#include "gemm_mx.h"
 #include "launch.hpp"
 
 using namespace tmm;
 
 namespace {
 
-constexpr int kVersion = 5;
+constexpr int kVersion = 6;
 constexpr int kDefaultCUs = 256;        // MI355X
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t k2G = int64_t(1) << 31;
@@ -396,6 +397,110 @@ int plan_into(int variant, const Shape& s, int num_cus, int* kernel_id, int64_t*
     return GEMM_OK;
 }
 
+// --- block-scaled 8-bit GEMM (gemm_mx) ------------------------------------------------------
+struct MxShape {
+    int fa, fb;
+    int64_t M, N, K;
+    const void *A, *SA, *B, *SB;
+    int64_t lda, ldsa, ldb, ldsb;
+    const void* C;
+    int64_t ldc;
+    int out;
+};
+
+int validate_mx(const MxShape& s) {
+    if (s.out != GEMM_OUT_FP32 && s.out != GEMM_OUT_BF16) return GEMM_ERR_DTYPE;
+    if ((s.fa != GEMM_MX_E4M3 && s.fa != GEMM_MX_E5M2) || (s.fb != GEMM_MX_E4M3 && s.fb != GEMM_MX_E5M2))
+        return GEMM_ERR_ARG;
+    if (s.M < 0 || s.N < 0 || s.K < 0 || s.K % 32) return GEMM_ERR_ARG;
+    const int64_t kb = std::max<int64_t>(s.K / 32, 1);
+    if (s.lda < std::max<int64_t>(s.K, 1) || s.ldb < std::max<int64_t>(s.K, 1) || s.ldsa < kb || s.ldsb < kb ||
+        s.ldc < std::max<int64_t>(s.N, 1))
+        return GEMM_ERR_ARG;
+    if (cdiv(s.M, 64) > 65535 || cdiv(s.N, 64) >= k2G) return GEMM_ERR_ARG;
+    if (static_cast<__int128>(s.M) * s.lda >= (int64_t(1) << 62) ||
+        static_cast<__int128>(s.N) * s.ldb >= (int64_t(1) << 62))
+        return GEMM_ERR_ARG;
+    if (s.M > 0 && s.N > 0 && s.C == nullptr) return GEMM_ERR_NULL;
+    if (s.K > 0 && s.M > 0 && s.N > 0 &&
+        (s.A == nullptr || s.SA == nullptr || s.B == nullptr || s.SB == nullptr))
+        return GEMM_ERR_NULL;
+    return GEMM_OK;
+}
+
+// Preconditions of the scaled-MFMA ring kernel: whole 128-deep blocks, 4-byte aligned rows of
+// the operands (16-byte direct-to-LDS loads) and of the scales (dword loads), tile extents
+// addressable by 32-bit buffer offsets.
+bool mx_ring_ok(const MxShape& s) {
+    if (s.K % 128) return false;
+    if (!aligned(s.A, 4) || !aligned(s.B, 4) || !aligned(s.SA, 4) || !aligned(s.SB, 4)) return false;
+    if (s.lda % 4 || s.ldb % 4 || s.ldsa % 4 || s.ldsb % 4) return false;
+    return 256 * s.lda < k2G && 256 * s.ldb < k2G && 256 * s.ldsa < k2G && 256 * s.ldsb < k2G;
+}
+
+int plan_mx(int variant, const MxShape& s, int cus, Plan& p) {
+    if (variant < GEMM_MX_VARIANT_AUTO || variant > GEMM_MX_VARIANT_RING) return GEMM_ERR_ARG;
+    p = Plan{};
+    if (s.M == 0 || s.N == 0) {
+        p.kernel = K_NONE;
+        return GEMM_OK;
+    }
+    if (s.K == 0) {
+        p.kernel = K_ZERO_FILL;
+        p.grid_x = static_cast<int>(std::min<int64_t>(cdiv(s.M * s.N, 256), 65536));
+        p.grid_y = p.grid_z = 1;
+        p.block = 256;
+        return GEMM_OK;
+    }
+    const bool ring = mx_ring_ok(s);
+    if (variant == GEMM_MX_VARIANT_RING && !ring) return GEMM_ERR_UNSUPPORTED;
+    if (ring && variant != GEMM_MX_VARIANT_SIMPLE) {
+        p.kernel = K_MX_RING_256;
+        p.grid.tiles_m = static_cast<int>(cdiv(s.M, 256));
+        p.grid.tiles_n = static_cast<int>(cdiv(s.N, 256));
+        if (int64_t(p.grid.tiles_m) * p.grid.tiles_n >= k2G) return GEMM_ERR_UNSUPPORTED;
+        p.grid.total = p.grid.tiles_m * p.grid.tiles_n;
+        p.grid.group_m = 4;
+        p.grid_x = std::min(p.grid.total, cus);
+        p.grid_y = p.grid_z = 1;
+        p.block = 256;
+        const uintptr_t ca = s.out == GEMM_OUT_FP32 ? 16 : 8;
+        p.vec_store = aligned(s.C, ca) && s.ldc % 4 == 0;
+        return GEMM_OK;
+    }
+    p.kernel = K_MX_SIMPLE_64;
+    p.grid_x = static_cast<int>(cdiv(s.N, 64));
+    p.grid_y = static_cast<int>(cdiv(s.M, 64));
+    p.grid_z = 1;
+    p.block = 256;
+    return GEMM_OK;
+}
+
+int run_mx(int variant, const MxShape& s, void* stream) {
+    int rc = validate_mx(s);
+    if (rc != GEMM_OK) return rc;
+    if (s.M == 0 || s.N == 0) return GEMM_OK;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != GEMM_OK) return rc;
+    Plan p;
+    rc = plan_mx(variant, s, cus, p);
+    if (rc != GEMM_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (p.kernel == K_ZERO_FILL) {
+        GemmArgs g{1, s.M, s.N, 0, nullptr, 0, 0, nullptr, 0, 0, const_cast<void*>(s.C), s.ldc, 0};
+        e = launch_zero_fill(g, s.out, p, st);
+    } else {
+        MxArgs g{s.M, s.N, s.K,
+                 static_cast<const uint8_t*>(s.A), s.lda, static_cast<const uint8_t*>(s.SA), s.ldsa,
+                 static_cast<const uint8_t*>(s.B), s.ldb, static_cast<const uint8_t*>(s.SB), s.ldsb,
+                 const_cast<void*>(s.C), s.ldc, s.fa, s.fb};
+        e = launch_mx(g, s.out, p, st);
+    }
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -489,6 +594,48 @@ int gemm_bf16_splitk_plan(int a_layout, int b_layout, int splits, int64_t batch,
     return GEMM_OK;
 }
 
+int gemm_mx(int a_format, int b_format, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+            const void* A_scale, int64_t lda_scale, const void* B, int64_t ldb, const void* B_scale,
+            int64_t ldb_scale, void* C, int64_t ldc, int out_dtype, void* stream) {
+    return run_mx(GEMM_MX_VARIANT_AUTO,
+                  MxShape{a_format, b_format, M, N, K, A, A_scale, B, B_scale, lda, lda_scale, ldb, ldb_scale, C,
+                          ldc, out_dtype},
+                  stream);
+}
+
+int gemm_mx_variant(int variant, int a_format, int b_format, int64_t M, int64_t N, int64_t K, const void* A,
+                    int64_t lda, const void* A_scale, int64_t lda_scale, const void* B, int64_t ldb,
+                    const void* B_scale, int64_t ldb_scale, void* C, int64_t ldc, int out_dtype, void* stream) {
+    return run_mx(variant,
+                  MxShape{a_format, b_format, M, N, K, A, A_scale, B, B_scale, lda, lda_scale, ldb, ldb_scale, C,
+                          ldc, out_dtype},
+                  stream);
+}
+
+int gemm_mx_validate(int a_format, int b_format, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                     const void* A_scale, int64_t lda_scale, const void* B, int64_t ldb, const void* B_scale,
+                     int64_t ldb_scale, const void* C, int64_t ldc, int out_dtype) {
+    return validate_mx(MxShape{a_format, b_format, M, N, K, A, A_scale, B, B_scale, lda, lda_scale, ldb,
+                               ldb_scale, C, ldc, out_dtype});
+}
+
+int gemm_mx_plan(int variant, int a_format, int b_format, int64_t M, int64_t N, int64_t K, const void* A,
+                 int64_t lda, const void* A_scale, int64_t lda_scale, const void* B, int64_t ldb,
+                 const void* B_scale, int64_t ldb_scale, const void* C, int64_t ldc, int out_dtype, int num_cus,
+                 int* kernel_id, int64_t* grid_x, int* block) {
+    const MxShape s{a_format, b_format, M, N, K, A, A_scale, B, B_scale, lda, lda_scale, ldb, ldb_scale, C,
+                    ldc, out_dtype};
+    int rc = validate_mx(s);
+    if (rc != GEMM_OK) return rc;
+    Plan p;
+    rc = plan_mx(variant, s, num_cus > 0 ? num_cus : kDefaultCUs, p);
+    if (rc != GEMM_OK) return rc;
+    if (kernel_id) *kernel_id = p.kernel;
+    if (grid_x) *grid_x = int64_t(p.grid_x) * (p.grid_y ? p.grid_y : 1) * (p.grid_z ? p.grid_z : 1);
+    if (block) *block = p.block;
+    return GEMM_OK;
+}
+
 const char* gemm_bf16_kernel_name(int k) {
     switch (k) {
         case K_NONE: return "none";
@@ -503,6 +650,8 @@ const char* gemm_bf16_kernel_name(int k) {
         case K_PINGPONG_256: return "pingpong_256";
         case K_RING8_256: return "ring8_256";
         case K_RING4_256: return "ring4_256";
+        case K_MX_RING_256: return "mx_ring_256";
+        case K_MX_SIMPLE_64: return "mx_simple_64";
         case K_GEMV: return "gemv";
         case K_GEMV_LDS: return "gemv_lds";
         default: return "?";

@@ -24,7 +24,9 @@ enum KernelId {
     K_PINGPONG_256 = 11,    // ladder steps 7-9: two wave groups alternate load and MFMA phases
     K_RING8_256 = 12,       // steps 4-6 with a five-slot 32-deep ring, loads spread over the K loop; 8 waves
     K_RING4_256 = 13,       //   same, 4 waves of 128 x 128 (AGPR accumulators)
-    K_COUNT = 14
+    K_MX_RING_256 = 14,     // block-scaled 8-bit GEMM: the 4-wave ring with scaled MFMAs
+    K_MX_SIMPLE_64 = 15,    //   general fallback (any K multiple of 32, pitch, alignment)
+    K_COUNT = 16
 };
 
 // Launch shape chosen for a problem (filled by the planner, consumed by the launchers).
@@ -44,6 +46,7 @@ hipError_t launch_pingpong(const GemmArgs& g, int out, const Plan& p, hipStream_
 hipError_t launch_ring(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs& g, int out, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_mx(const MxArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_gemv_lds(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 int gemv_lds_rows_per_workgroup();
 int gemv_lds_threads();

@@ -214,3 +214,99 @@ def make_operands(name: str, item: int = 0, lda=None, ldb=None, rows=None, row_o
     A = operand(w["a"][0], M, w["K"], sa, w["a"][1], lda, row_offset=row_offset)
     B = operand(w["b"][0], w["N"], w["K"], sb, w["b"][1], ldb)
     return A, B
+
+
+# ---------------------------------------------------------------------------------------
+# Block-scaled 8-bit operands (gemm_mx): element codes (uint8) and one E8M0 scale code per
+# 32 consecutive columns.  Values are drawn as above and quantised per block of 32 the way
+# the OCP microscaling format describes: shared exponent X = floor(log2(max |v|)) - emax of
+# the element format (8 for E4M3, 15 for E5M2), scale code X + 127 (clamped to 0 .. 254),
+# elements v / 2^X rounded to nearest even in the element format, saturating at its largest
+# finite value.  Padding columns hold a NaN code (and padding scale columns 0xFF, NaN), so a
+# kernel that reads them fails the check.
+# ---------------------------------------------------------------------------------------
+MX_E4M3, MX_E5M2 = 0, 1
+_MX_EMAX = {MX_E4M3: 8, MX_E5M2: 15}
+_MX_MAX = {MX_E4M3: 448.0, MX_E5M2: 57344.0}
+MX_PAD_CODE = 0x7F        # NaN in both formats
+MX_PAD_SCALE = 0xFF       # NaN scale
+
+
+def fp8_codes(x: np.ndarray, fmt: int) -> np.ndarray:
+    """float values -> 8-bit codes (round to nearest even, saturating)."""
+    import torch
+    dt = torch.float8_e4m3fn if fmt == MX_E4M3 else torch.float8_e5m2
+    m = _MX_MAX[fmt]
+    x32 = np.clip(np.asarray(x, dtype=np.float64), -m, m).astype(np.float32)
+    return torch.from_numpy(np.ascontiguousarray(x32)).to(dt).view(torch.uint8).numpy()
+
+
+def _mx_pad(rows, cols, ld, lds):
+    ld = cols if ld is None else ld
+    lds = cols // 32 if lds is None else lds
+    if cols % 32:
+        raise ValueError("columns must be a multiple of 32")
+    if ld < cols or lds < cols // 32:
+        raise ValueError("pitch below the extent")
+    return (np.full((rows, ld), MX_PAD_CODE, dtype=np.uint8),
+            np.full((rows, lds), MX_PAD_SCALE, dtype=np.uint8))
+
+
+def mx_operand(kind: str, rows: int, cols: int, seed: int, fmt: int, params=(), ld=None,
+               lds=None, row_offset: int = 0):
+    """(codes rows x ld, scales rows x lds) of ``kind`` values quantised to the MX format."""
+    codes, scales = _mx_pad(rows, cols, ld, lds)
+    if rows == 0 or cols == 0:
+        return codes, scales
+    rows_per_chunk = max(1, _CHUNK // cols)
+    w = _Work(min(rows, rows_per_chunk) * cols)
+    for r0 in range(0, rows, rows_per_chunk):
+        r1 = min(rows, r0 + rows_per_chunk)
+        v = _values(kind, seed, (row_offset + r0) * cols, (r1 - r0) * cols, params, w)
+        blk = v.reshape(r1 - r0, cols // 32, 32)
+        amax = np.abs(blk).max(axis=2)
+        with np.errstate(divide="ignore"):
+            X = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - _MX_EMAX[fmt]
+        X = np.where(amax > 0, X, -127.0)
+        sc = np.clip(X + 127, 0, 254)
+        q = blk / np.exp2(sc - 127)[:, :, None]
+        codes[r0:r1, :cols] = fp8_codes(q.reshape(r1 - r0, cols), fmt)
+        scales[r0:r1, :cols // 32] = sc.astype(np.uint8)
+    return codes, scales
+
+
+def mx_integers(rows: int, cols: int, seed: int, fmt: int, lo=-4, hi=4, scale_lo=126,
+                scale_hi=128, ld=None, lds=None):
+    """Integer elements in [lo, hi] (exact in both formats for |v| <= 4) and scale codes in
+    [scale_lo, scale_hi], each from its own counter stream."""
+    codes, scales = _mx_pad(rows, cols, ld, lds)
+    if rows == 0 or cols == 0:
+        return codes, scales
+    v = _values("integer", seed, 0, rows * cols, (lo, hi)).reshape(rows, cols)
+    codes[:, :cols] = fp8_codes(v, fmt)
+    s = _values("integer", seed + 7919, 0, rows * (cols // 32), (scale_lo, scale_hi))
+    scales[:, :cols // 32] = s.reshape(rows, cols // 32).astype(np.uint8)
+    return codes, scales
+
+
+# Workloads of the block-scaled GEMM: the square and FFN shapes above with the same value
+# distributions, quantised to MXFP8.
+MX_WORKLOADS = {
+    "mx_e4m3_square_4096": dict(cfg=2, M=4096, N=4096, K=4096, fa=MX_E4M3, fb=MX_E4M3,
+                                a=("normal", (1.0,)), b=("normal", (1.0,)), out=OUT_FP32),
+    "mx_e5m2_e4m3_square_4096": dict(cfg=2, M=4096, N=4096, K=4096, fa=MX_E5M2, fb=MX_E4M3,
+                                     a=("normal", (1.0,)), b=("normal", (1.0,)), out=OUT_FP32),
+    "mx_e4m3_ffn_up_8192x14336x4096": dict(cfg=4, M=8192, N=14336, K=4096, fa=MX_E4M3,
+                                           fb=MX_E4M3, a=("normal", (1.0,)),
+                                           b=("normal", (0.02,)), out=OUT_BF16),
+}
+
+
+def make_mx_operands(name: str, rows=None, row_offset=0):
+    """(A, SA, B, SB) of MX workload ``name``; ``rows``/``row_offset`` select a band of A."""
+    w = MX_WORKLOADS[name]
+    sa, sb = seeds(w["cfg"])
+    M = w["M"] if rows is None else rows
+    A, SA = mx_operand(w["a"][0], M, w["K"], sa, w["fa"], w["a"][1], row_offset=row_offset)
+    B, SB = mx_operand(w["b"][0], w["N"], w["K"], sb, w["fb"], w["b"][1])
+    return A, SA, B, SB
