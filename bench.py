@@ -178,6 +178,56 @@ def gemm_leg(args, torch):
     }
 
 
+FP8_MFMA_TFLOPS = 5000.0   # MI355X dense fp8 (MXFP8) MFMA peak
+
+
+def mx_leg(args, torch):
+    """The block-scaled 8-bit GEMM (gemm_mx) on an MX workload, rotating input sets."""
+    name = args.workload
+    w = synth.MX_WORKLOADS[name]
+    M, N, K, fa, fb, out = w["M"], w["N"], w["K"], w["fa"], w["fb"], w["out"]
+    log(f"[bench] generating {name} operands")
+    A, SA, B, SB = synth.make_mx_operands(name)
+    per = A.size + SA.size + B.size + SB.size + M * N * (4 if out == tm.GEMM_OUT_FP32 else 2)
+    nsets = max(1, -(-(args.rotate_mb * 2 ** 20) // per))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    base = [dev(A), dev(SA), dev(B), dev(SB)]
+    out_t = torch.float32 if out == tm.GEMM_OUT_FP32 else torch.bfloat16
+    sets = [([t if i == 0 else t.clone() for t in base]) + [torch.empty((M, N), dtype=out_t, device="cuda")]
+            for i in range(nsets)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    a, sa, b, sb, c = sets[0]
+    rc, kname, grid, block = tm.gemm_mx_plan(0, fa, fb, M, N, K, a, K, sa, K // 32, b, K, sb, K // 32,
+                                             c, N, out, cus)
+    if rc != 0:
+        raise SystemExit(f"gemm_mx cannot run {name}: {tm.gemm_bf16_status_string(rc)}")
+
+    def launch(i):
+        a, sa, b, sb, c = sets[i]
+        tm.gemm_mx(fa, fb, M, N, K, a, K, sa, K // 32, b, K, sb, K // 32, c, N, out)
+
+    log(f"[bench] timing {name}: kernel {kname}, {nsets} rotating buffer sets, "
+        f"{args.warmup} warm-up + {args.steps} timed steps")
+    ms, wall = time_steps(launch, nsets, args.steps, args.warmup, torch)
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms * 1e-3) / 1e12
+    fmt = {0: "e4m3", 1: "e5m2"}
+    return {
+        "metric": "MXFP8 GEMM TFLOP/s (block-scaled 8-bit, fp32 accumulate)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": f"mx-{fmt[fa]}x{fmt[fb]}", "data": "synthetic",
+        "config": {"workload": f"{name}: C = A B^T, M={M} N={N} K={K}, A {fmt[fa]} and B "
+                               f"{fmt[fb]} with E8M0 scales per 32 k, fp32 accumulate, "
+                               f"{'fp32' if out == 0 else 'bf16'} out",
+                   "kernel": kname, "grid": grid, "block": block, "rotating_buffer_sets": nsets},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP8_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / FP8_MFMA_TFLOPS,
+                     "traffic": traffic_for(kname, name), "flops_per_launch": flops},
+        "kernel_source_sha": kernel_source_sha(),
+    }
+
+
 def gemm_roofline(res):
     """The roof that binds this workload (by its arithmetic intensity against the ridge) and
     the achieved rate against it."""
@@ -304,7 +354,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="square_4096", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default="square_4096",
+                    choices=sorted(synth.WORKLOADS) + sorted(synth.MX_WORKLOADS))
     ap.add_argument("--variant", default="auto", choices=sorted(tm.VARIANTS))
     ap.add_argument("--a-layout", default="k", choices=["k", "mn"],
                     help="A stored M x K (k) or K x M (mn)")
@@ -347,6 +398,9 @@ def main():
                           "kernel_source_sha": kernel_source_sha()}))
         return
 
+    if args.workload in synth.MX_WORKLOADS:
+        print(json.dumps(mx_leg(args, torch)))
+        return
     res = gemm_leg(args, torch)
     result = {
         "metric": "bf16 GEMM TFLOP/s + % MFMA peak at 4096^3; GB/s % HBM peak at M=1",

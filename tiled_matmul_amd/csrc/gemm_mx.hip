@@ -27,6 +27,11 @@
 
 namespace tmm {
 
+// MFMAs at the end of each k step that follow its last fragment read (see step()).
+#ifndef TMM_MX_TAIL
+#define TMM_MX_TAIL 8
+#endif
+
 namespace mx {
 constexpr int BM = 256, BN = 256, BKB = 128, NA = 3, NB = 2;   // BKB: bytes (= k) per block
 constexpr int ROWB = BKB;
@@ -146,14 +151,9 @@ __global__ __launch_bounds__(256, 1) void mx_ring_kernel(MxArgs g, TileGrid tg, 
                 sa[q - FN] = __builtin_amdgcn_raw_buffer_load_b32(rsa, j < nk ? sa0 + (q - FN) * sstrideA : OOB, soff, 0);
         };
         using F = MxFrags<FN, FM>;
-        // Read q of k step kk (q / 2: fragment, B first; q % 2: which 16 bytes).  With the
-        // first read the fragment takes scale byte lg of the set entry: for kk = 0 the entry
-        // still holds the loaded dword (bytes 0-3: 32-blocks 0-3 of the block) and is then
-        // shifted right by 16 in place, so that for kk = 1 byte lg is 32-block 2 + lg.  (The
-        // kk = 0 reads follow the wait that covers the set's loads; the in-place shift, as
-        // assembly that LLVM cannot fold into the kk = 1 shift, also tells it that the kk = 1
-        // reads depend on no load in flight.)
-        auto read_one = [&](F& f, int q, int at, int bt_, int kk, int (&sb)[FN], int (&sa)[FM]) {
+        // Read q of k step kk (q / 2: fragment, B first; q % 2: which 16 bytes); with the first
+        // read the fragment takes scale byte 2 kk + lg of its set entry.
+        auto read_one = [&](F& f, int q, int at, int bt_, int kk, const int (&sb)[FN], const int (&sa)[FM]) {
             const int fr = q / 2, e = q % 2;
             MxFrag& x = fr < FN ? f.b[fr] : f.a[fr - FN];
             const int base = fr < FN ? bt_ + b_off + 32 * fr * ROWB : at + a_off + 32 * (fr - FN) * ROWB;
@@ -161,12 +161,10 @@ __global__ __launch_bounds__(256, 1) void mx_ring_kernel(MxArgs g, TileGrid tg, 
 #pragma unroll
             for (int c = 0; c < 4; ++c) x.v[4 * e + c] = static_cast<int>(v[c]);
             if (e == 0) {
-                int& sref = fr < FN ? sb[fr] : sa[fr - FN];
-                x.s = static_cast<int>(static_cast<uint32_t>(sref) >> (8 * lg));
-                if (kk == 0) asm volatile("v_lshrrev_b32 %0, 16, %0" : "+v"(sref));   // not folded
+                const int s = fr < FN ? sb[fr] : sa[fr - FN];
+                x.s = static_cast<int>(static_cast<uint32_t>(s) >> (8 * (2 * kk + lg)));
             }
         };
-
         Acc acc[FN][FM];
 #pragma unroll
         for (int i = 0; i < FN; ++i)
@@ -206,17 +204,18 @@ __global__ __launch_bounds__(256, 1) void mx_ring_kernel(MxArgs g, TileGrid tg, 
         int a0 = 0, a1 = TILE, a2 = 2 * TILE, b0 = B_BASE, b1 = B_BASE + TILE;
         // One iteration on block b with its scales in (sbC, saC) and block b+1's in (sbN, saN).
         auto iteration = [&](int b, int (&sbC)[FN], int (&saC)[FM], int (&sbN)[FN], int (&saN)[FM]) {
-            step<FN, FM, NR, L, true, MM, 8>(acc, f[0], [&](int q) { read_one(f[1], q, a0, b0, 1, sbC, saC); },
+            step<FN, FM, NR, L, true, MM, TMM_MX_TAIL>(acc, f[0], [&](int q) { read_one(f[1], q, a0, b0, 1, sbC, saC); },
                                              [&](int q) { load_one(true, q, b + 2, a2); });
             wait_cnt<L, 0>();   // all but this step's A(b+2) loads: B(b+1), scales(b+1) landed
             barrier();
-            step<FN, FM, NR, L + FN + FM, true, MM, 8>(
+            step<FN, FM, NR, L + FN + FM, true, MM, TMM_MX_TAIL>(
                 acc, f[1], [&](int q) { read_one(f[0], q, a1, b1, 0, sbN, saN); },
                 [&](int q) {
-                    if (q < L)
-                        load_one(false, q, b + 2, b0);
+                    // scales first: a wait LLVM places for them then leaves the B loads in flight
+                    if (q < FN + FM)
+                        load_scales(q, b + 2, sbC, saC);
                     else
-                        load_scales(q - L, b + 2, sbC, saC);
+                        load_one(false, q - (FN + FM), b + 2, b0);
                 });
             __builtin_amdgcn_sched_barrier(0);
             wait_cnt<63, 0>();
