@@ -135,3 +135,48 @@ def check_mx(C, C_ref: np.ndarray, Mag: np.ndarray, F: np.ndarray, K: int, out_d
         "max_err_over_bound": float(ratio.max()) if ratio.size else 0.0,
         "max_abs_err": float(err[finite].max()) if finite.any() else 0.0,
     }
+
+
+def attention_row_delta(SMAG: np.ndarray) -> np.ndarray:
+    """Bound on the fp32 error of every score of a row and of its exp argument (see
+    check_attention), from the oracle's SMAG."""
+    return 2.0 ** -22 * SMAG + 2.0 ** -20
+
+
+def check_attention(O, O_ref, PV, SMAG, Lk: int, out_dtype: int, LSE=None, LSE_ref=None) -> dict:
+    """Acceptance check of the attention forward against oracle/attention.py.
+
+    Derivation (kernel arithmetic: scores from exact bf16 products accumulated in fp32; exp in
+    fp32; the unnormalised probabilities rounded to bf16 for the second product, whose sums are
+    fp32; one fp32 division per row).  A score error of at most delta (fp32 accumulation of d
+    products, the scale, and the exp argument: attention_row_delta) scales each probability by
+    at most e^(2 delta); rounding a probability to bf16 changes it by at most 2^-8 of itself; the
+    fp32 sums over Lk keys add Lk 2^-24 relative.  So with PV = P |V|:
+
+        fp32 output:  |O - O_ref| <= t = (2^-8 + 4 delta + 2 Lk 2^-24 + 2^-20) PV
+        bf16 output:  |O - O_ref| <= t + 2^-8 (|O_ref| + t)
+        LSE:          |LSE - LSE_ref| <= 2 delta + Lk 2^-23   (both -inf for an empty row)
+    """
+    delta = attention_row_delta(SMAG)[..., None]
+    t = (2.0 ** -8 + 4 * delta + 2 * Lk * 2.0 ** -24 + 2.0 ** -20) * PV
+    if out_dtype == OUT_BF16:
+        t = t + 2.0 ** -8 * (np.abs(O_ref) + t)
+    Og = to_f64(O, out_dtype)
+    err = np.abs(Og - O_ref)
+    finite = np.isfinite(Og)
+    bad = ~finite | (err > t)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(t > 0, err / np.where(t > 0, t, 1.0), np.where(err > 0, np.inf, 0.0))
+    ratio = np.where(finite, ratio, np.inf)
+    r = {"ok": bool(not bad.any()), "n": int(Og.size), "n_fail": int(bad.sum()),
+         "max_err_over_bound": float(ratio.max()) if ratio.size else 0.0}
+    if LSE is not None:
+        L = np.asarray(LSE, dtype=np.float64)
+        both_inf = np.isneginf(L) & np.isneginf(LSE_ref)
+        lb = 2 * attention_row_delta(SMAG) + Lk * 2.0 ** -23
+        le = np.where(both_inf, 0.0, np.abs(L - LSE_ref))
+        lbad = ~(both_inf | (np.isfinite(L) & (le <= lb)))
+        r["lse_ok"] = bool(not lbad.any())
+        r["lse_max_err_over_bound"] = float(np.max(np.where(lb > 0, le / lb, 0.0))) if L.size else 0.0
+        r["ok"] = r["ok"] and r["lse_ok"]
+    return r
