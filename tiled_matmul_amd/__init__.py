@@ -20,7 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # tile-shape macros by tiled_matmul_amd.build.build_library(out=..., defines=...)).
 LIB_PATH = os.environ.get("GEMM_BF16_LIB") or os.path.join(_HERE, "libgemm_bf16.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gemm_bf16.h")
-HEADERS = [HEADER, os.path.join(os.path.dirname(_HERE), "include", "gemm_mx.h")]
+HEADERS = [HEADER, os.path.join(os.path.dirname(_HERE), "include", "gemm_mx.h"),
+           os.path.join(os.path.dirname(_HERE), "include", "attention.h")]
 
 GEMM_OK = 0
 GEMM_ERR_ARG = 1
@@ -42,6 +43,11 @@ GEMM_MX_E5M2 = 1
 GEMM_MX_VARIANT_AUTO = 0
 GEMM_MX_VARIANT_SIMPLE = 1
 GEMM_MX_VARIANT_RING = 2
+
+# Attention forward (include/attention.h)
+ATTN_VARIANT_AUTO = 0
+ATTN_VARIANT_SIMPLE = 1
+ATTN_VARIANT_MFMA = 2
 
 GEMM_VARIANT_AUTO = 0
 GEMM_VARIANT_SIMPLE = 1
@@ -103,7 +109,15 @@ def _load():
     lib.gemm_mx_validate.argtypes = mx
     lib.gemm_mx_plan.argtypes = [_int] + mx + [_int, ctypes.POINTER(_int), ctypes.POINTER(_i64),
                                                 ctypes.POINTER(_int)]
-    for f in ("gemm_mx", "gemm_mx_variant", "gemm_mx_validate", "gemm_mx_plan"):
+    at = [_i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
+    lib.attention_fwd.argtypes = at + [_vp, ctypes.c_float, _int, _int, _vp]
+    lib.attention_fwd_variant.argtypes = [_int] + at + [_vp, ctypes.c_float, _int, _int, _vp]
+    lib.attention_fwd_validate.argtypes = at + [ctypes.c_float, _int, _int]
+    lib.attention_fwd_plan.argtypes = [_int] + at + [ctypes.c_float, _int, _int, _int,
+                                                     ctypes.POINTER(_int), ctypes.POINTER(_i64),
+                                                     ctypes.POINTER(_int)]
+    for f in ("gemm_mx", "gemm_mx_variant", "gemm_mx_validate", "gemm_mx_plan", "attention_fwd",
+              "attention_fwd_variant", "attention_fwd_validate", "attention_fwd_plan"):
         getattr(lib, f).restype = _int
     for f in ("gemm_bf16", "gemm_bf16_strided_batched", "gemm_bf16_variant",
               "gemm_bf16_validate", "gemm_bf16_plan", "gemm_bf16_version", "gemm_bf16_layout",
@@ -128,7 +142,8 @@ def declared_functions() -> list[str]:
     names = set()
     for h in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gemm_\w*)\s*\(", text, re.M))
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:gemm|attention)_\w*)\s*\(",
+                                text, re.M))
     return sorted(names)
 
 
@@ -270,6 +285,34 @@ def gemm_mx_plan(variant, a_format, b_format, M, N, K, A, lda, A_scale, lda_scal
                               lda_scale, _ptr(B), ldb, _ptr(B_scale), ldb_scale, _ptr(C), ldc,
                               out_dtype, num_cus, ctypes.byref(k), ctypes.byref(g),
                               ctypes.byref(b))
+    return rc, gemm_bf16_kernel_name(k.value), g.value, b.value
+
+
+def attention_fwd(B, Hq, Hkv, Lq, Lk, d, Q, K, V, O, LSE, scale, causal, out_dtype, stream=None):
+    _check(_load().attention_fwd(B, Hq, Hkv, Lq, Lk, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                 _ptr(LSE), scale, int(causal), out_dtype, _stream(stream)),
+           "attention_fwd")
+
+
+def attention_fwd_variant(variant, B, Hq, Hkv, Lq, Lk, d, Q, K, V, O, LSE, scale, causal,
+                          out_dtype, stream=None):
+    _check(_load().attention_fwd_variant(variant, B, Hq, Hkv, Lq, Lk, d, _ptr(Q), _ptr(K),
+                                         _ptr(V), _ptr(O), _ptr(LSE), scale, int(causal),
+                                         out_dtype, _stream(stream)), "attention_fwd_variant")
+
+
+def attention_fwd_validate(B, Hq, Hkv, Lq, Lk, d, Q, K, V, O, scale, causal, out_dtype) -> int:
+    return _load().attention_fwd_validate(B, Hq, Hkv, Lq, Lk, d, _ptr(Q), _ptr(K), _ptr(V),
+                                          _ptr(O), scale, int(causal), out_dtype)
+
+
+def attention_fwd_plan(variant, B, Hq, Hkv, Lq, Lk, d, Q, K, V, O, scale, causal, out_dtype,
+                       num_cus=0):
+    """(status, kernel_name, workgroups, threads_per_workgroup)."""
+    k, g, b = _int(0), _i64(0), _int(0)
+    rc = _load().attention_fwd_plan(variant, B, Hq, Hkv, Lq, Lk, d, _ptr(Q), _ptr(K), _ptr(V),
+                                    _ptr(O), scale, int(causal), out_dtype, num_cus,
+                                    ctypes.byref(k), ctypes.byref(g), ctypes.byref(b))
     return rc, gemm_bf16_kernel_name(k.value), g.value, b.value
 
 

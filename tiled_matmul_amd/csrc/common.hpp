@@ -54,6 +54,18 @@ struct MxArgs {
     int fa, fb;
 };
 
+// Attention forward (attention_fwd): [B][H][L][d] bf16 tensors, contiguous.
+struct AttnArgs {
+    int64_t B, Hq, Hkv, Lq, Lk, d;
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* V;
+    void* O;
+    float* LSE;
+    float scale;
+    int causal;
+};
+
 struct TileGrid {
     int tiles_m, tiles_n, total, group_m;
 };

@@ -6,13 +6,15 @@
 
 #include "gemm_bf16.h"
 #include "gemm_mx.h"
+#include "attention.h"
 #include "launch.hpp"
+#include <math.h>
 
 using namespace tmm;
 
 namespace {
 
-constexpr int kVersion = 6;
+constexpr int kVersion = 7;
 constexpr int kDefaultCUs = 256;        // MI355X
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t k2G = int64_t(1) << 31;
@@ -501,6 +503,72 @@ int run_mx(int variant, const MxShape& s, void* stream) {
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// --- attention forward (attention_fwd) ---------------------------------------------------
+struct AttnShape {
+    int64_t B, Hq, Hkv, Lq, Lk, d;
+    const void *Q, *K, *V, *O;
+    float scale;
+    int causal, out;
+};
+
+int validate_attn(const AttnShape& s) {
+    if (s.out != GEMM_OUT_FP32 && s.out != GEMM_OUT_BF16) return GEMM_ERR_DTYPE;
+    if (s.B < 1 || s.B > 65535 || s.Hq < 1 || s.Hq > 65535 || s.Hkv < 1 || s.Hq % s.Hkv) return GEMM_ERR_ARG;
+    if (s.Lq < 0 || s.Lk < 0 || s.d < 8 || s.d > 256 || s.d % 8) return GEMM_ERR_ARG;
+    if (s.causal != 0 && s.causal != 1) return GEMM_ERR_ARG;
+    if (!std::isfinite(s.scale)) return GEMM_ERR_ARG;
+    // every element index fits comfortably in int64 and the query blocks in a grid dimension
+    if (static_cast<__int128>(s.B) * s.Hq * std::max<int64_t>(s.Lq, s.Lk) * s.d >= (int64_t(1) << 62)) return GEMM_ERR_ARG;
+    if (cdiv(s.Lq, 4) >= k2G) return GEMM_ERR_ARG;
+    if (s.Lq > 0 && (s.Q == nullptr || s.O == nullptr)) return GEMM_ERR_NULL;
+    if (s.Lq > 0 && s.Lk > 0 && (s.K == nullptr || s.V == nullptr)) return GEMM_ERR_NULL;
+    return GEMM_OK;
+}
+
+bool attn_mfma_ok(const AttnShape& s) {
+    (void)s;
+    return false;   // the MFMA kernel is not built yet
+}
+
+int plan_attn(int variant, const AttnShape& s, int cus, Plan& p) {
+    (void)cus;
+    if (variant < ATTN_VARIANT_AUTO || variant > ATTN_VARIANT_MFMA) return GEMM_ERR_ARG;
+    p = Plan{};
+    if (s.Lq == 0) {
+        p.kernel = K_NONE;
+        return GEMM_OK;
+    }
+    const bool mfma = attn_mfma_ok(s);
+    if (variant == ATTN_VARIANT_MFMA && !mfma) return GEMM_ERR_UNSUPPORTED;
+    if (mfma && variant != ATTN_VARIANT_SIMPLE) {
+        p.kernel = K_ATTN_MFMA;
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    p.kernel = K_ATTN_SIMPLE;
+    p.grid_x = static_cast<int>(cdiv(s.Lq, 4));
+    p.grid_y = static_cast<int>(s.Hq);
+    p.grid_z = static_cast<int>(s.B);
+    p.block = 256;
+    return GEMM_OK;
+}
+
+int run_attn(int variant, const AttnShape& s, float* lse, void* stream) {
+    int rc = validate_attn(s);
+    if (rc != GEMM_OK) return rc;
+    if (s.Lq == 0) return GEMM_OK;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != GEMM_OK) return rc;
+    Plan p;
+    rc = plan_attn(variant, s, cus, p);
+    if (rc != GEMM_OK) return rc;
+    AttnArgs g{s.B, s.Hq, s.Hkv, s.Lq, s.Lk, s.d,
+               static_cast<const uint16_t*>(s.Q), static_cast<const uint16_t*>(s.K),
+               static_cast<const uint16_t*>(s.V), const_cast<void*>(s.O), lse, s.scale, s.causal};
+    hipError_t e = launch_attention(g, s.out, p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -636,6 +704,39 @@ int gemm_mx_plan(int variant, int a_format, int b_format, int64_t M, int64_t N, 
     return GEMM_OK;
 }
 
+int attention_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d, const void* Q,
+                  const void* K, const void* V, void* O, float* LSE, float scale, int causal, int out_dtype,
+                  void* stream) {
+    return run_attn(ATTN_VARIANT_AUTO, AttnShape{B, Hq, Hkv, Lq, Lk, d, Q, K, V, O, scale, causal, out_dtype}, LSE,
+                    stream);
+}
+
+int attention_fwd_variant(int variant, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d,
+                          const void* Q, const void* K, const void* V, void* O, float* LSE, float scale, int causal,
+                          int out_dtype, void* stream) {
+    return run_attn(variant, AttnShape{B, Hq, Hkv, Lq, Lk, d, Q, K, V, O, scale, causal, out_dtype}, LSE, stream);
+}
+
+int attention_fwd_validate(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d, const void* Q,
+                           const void* K, const void* V, const void* O, float scale, int causal, int out_dtype) {
+    return validate_attn(AttnShape{B, Hq, Hkv, Lq, Lk, d, Q, K, V, O, scale, causal, out_dtype});
+}
+
+int attention_fwd_plan(int variant, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d,
+                       const void* Q, const void* K, const void* V, const void* O, float scale, int causal,
+                       int out_dtype, int num_cus, int* kernel_id, int64_t* grid_x, int* block) {
+    const AttnShape s{B, Hq, Hkv, Lq, Lk, d, Q, K, V, O, scale, causal, out_dtype};
+    int rc = validate_attn(s);
+    if (rc != GEMM_OK) return rc;
+    Plan p;
+    rc = plan_attn(variant, s, num_cus > 0 ? num_cus : kDefaultCUs, p);
+    if (rc != GEMM_OK) return rc;
+    if (kernel_id) *kernel_id = p.kernel;
+    if (grid_x) *grid_x = int64_t(p.grid_x) * (p.grid_y ? p.grid_y : 1) * (p.grid_z ? p.grid_z : 1);
+    if (block) *block = p.block;
+    return GEMM_OK;
+}
+
 const char* gemm_bf16_kernel_name(int k) {
     switch (k) {
         case K_NONE: return "none";
@@ -652,6 +753,8 @@ const char* gemm_bf16_kernel_name(int k) {
         case K_RING4_256: return "ring4_256";
         case K_MX_RING_256: return "mx_ring_256";
         case K_MX_SIMPLE_64: return "mx_simple_64";
+        case K_ATTN_SIMPLE: return "attn_simple";
+        case K_ATTN_MFMA: return "attn_mfma";
         case K_GEMV: return "gemv";
         case K_GEMV_LDS: return "gemv_lds";
         default: return "?";

@@ -26,7 +26,9 @@ enum KernelId {
     K_RING4_256 = 13,       //   same, 4 waves of 128 x 128 (AGPR accumulators)
     K_MX_RING_256 = 14,     // block-scaled 8-bit GEMM: the 4-wave ring with scaled MFMAs
     K_MX_SIMPLE_64 = 15,    //   general fallback (any K multiple of 32, pitch, alignment)
-    K_COUNT = 16
+    K_ATTN_SIMPLE = 16,     // attention forward: one wave per query row (any d <= 256)
+    K_ATTN_MFMA = 17,       //   MFMA tiles of queries x keys, online softmax (d = 64, 128)
+    K_COUNT = 18
 };
 
 // Launch shape chosen for a problem (filled by the planner, consumed by the launchers).
@@ -47,6 +49,7 @@ hipError_t launch_ring(const GemmArgs& g, int out, const Plan& p, hipStream_t s)
 hipError_t launch_splitk_reduce(const GemmArgs& g, int out, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_mx(const MxArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_gemv_lds(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 int gemv_lds_rows_per_workgroup();
 int gemv_lds_threads();

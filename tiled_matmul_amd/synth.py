@@ -310,3 +310,25 @@ def make_mx_operands(name: str, rows=None, row_offset=0):
     A, SA = mx_operand(w["a"][0], M, w["K"], sa, w["fa"], w["a"][1], row_offset=row_offset)
     B, SB = mx_operand(w["b"][0], w["N"], w["K"], sb, w["fb"], w["b"][1])
     return A, SA, B, SB
+
+
+# Attention forward workloads: [B][H][L][d] bf16 tensors of N(0,1) values (Q, K, V from their
+# own seeds), scale 1/sqrt(d).  A 4096-token causal prefill with grouped-query heads (32 query
+# heads over 8 key/value heads, d = 128) and a full (unmasked) attention with d = 64.
+ATTN_WORKLOADS = {
+    "attn_prefill_b1_h32_kv8_l4096_d128": dict(B=1, Hq=32, Hkv=8, Lq=4096, Lk=4096, d=128,
+                                               causal=True, scale=128 ** -0.5, out=OUT_BF16,
+                                               seed=6000),
+    "attn_full_b2_h16_l2048_d64": dict(B=2, Hq=16, Hkv=16, Lq=2048, Lk=2048, d=64,
+                                       causal=False, scale=64 ** -0.5, out=OUT_FP32, seed=6100),
+}
+
+
+def make_attention_inputs(name: str):
+    """(Q, K, V) bf16 bit arrays of attention workload ``name``."""
+    w = ATTN_WORKLOADS[name]
+    B, Hq, Hkv, Lq, Lk, d, s = w["B"], w["Hq"], w["Hkv"], w["Lq"], w["Lk"], w["d"], w["seed"]
+    Q = normal(B * Hq * Lq, d, s).reshape(B, Hq, Lq, d)
+    K = normal(B * Hkv * Lk, d, s + 1).reshape(B, Hkv, Lk, d)
+    V = normal(B * Hkv * Lk, d, s + 2).reshape(B, Hkv, Lk, d)
+    return Q, K, V
