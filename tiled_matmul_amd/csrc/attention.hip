@@ -10,6 +10,27 @@
 // (dot product over d from the row of Q staged in LDS), the wave takes the step's maximum and
 // sum, and each lane accumulates d / 64 output columns over the step's keys.  Any d <= 256
 // (d % 8 == 0); the general path and the reference the faster kernel is tested beside.
+//
+// attn_mfma_kernel (d = 64 or 128): a workgroup of 4 waves takes 128 query rows of one head
+// (32 per wave) and visits the keys in blocks of 64, K and V tiles staged in LDS by
+// direct-to-LDS loads (two buffers: block b+1 loads while block b is used).  Per block and
+// wave, with v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T: the key tile is the first operand and the wave's Q rows (held in registers
+//     for the whole loop) the second, so each lane ends with one query (lane mod 16) and 4
+//     keys (4 (lane / 16) + r) of each 16-key tile: the online-softmax maximum and sum of a
+//     query are an in-lane reduction over 16 values and two exchanges across lane groups.
+//   P = exp(S - m), rounded to bf16, is the second operand of O^T = V^T P^T as it stands in
+//     the accumulators: for a 32-key step (tiles t0, t1) lane group g holds keys 16 t0 + 4 g
+//     + (0..3) and 16 t1 + 4 g + (0..3), which is taken as the step's k order; the V^T operand
+//     follows the same order: two ds_read_b64_tr_b16 per fragment, each giving a lane 4
+//     consecutive keys of one head-dim column (the transposing read's lane layout: within 16
+//     lanes, lane i element e is element i mod 4 of the 8 bytes addressed by lane 4 e + i / 4).
+//   O^T accumulates in registers, rescaled by exp(m_old - m_new) per query before the block's
+//     products; each lane ends with 4 consecutive head-dim values of one query (vector stores).
+// LDS rows are d * 2 bytes; 16-byte chunk c of K row r sits at c ^ (r mod 8) (the K fragment
+// reads, 16 rows of one chunk, hit distinct banks) and chunk c of V row r at c ^ 2 (r mod 4)
+// (a transposing read touches 16 rows, 32 bytes each: 4 rows per 128-byte bank row).
+// Scores and the exponent are in base 2 (scale log2(e) folded into the scores).
 #include <math.h>
 
 #include "launch.hpp"
@@ -96,12 +117,216 @@ __global__ __launch_bounds__(256) void attn_simple_kernel(AttnArgs g) {
     if (g.LSE && lane == 0) g.LSE[(b * g.Hq + h) * g.Lq + i] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
+namespace at {
+constexpr int BQ = 128, WQ = 32, BKV = 64;
+}
+
+template <int D, int OUT>
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
+    using namespace at;
+    constexpr int ROWB = D * 2;            // bytes per LDS row
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int TILE = BKV * ROWB;       // one K or V tile
+    constexpr int RPI = 1024 / ROWB;       // rows per 1 KB load instruction
+    constexpr int LPT = TILE / 1024 / 4;   // load instructions per wave per tile
+    constexpr int KS = D / 32;             // k steps of S^T
+    constexpr int DT = D / 16;             // 16-wide head-dim tiles of O^T
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][TILE];   // [buffer][K, V]
+
+    const int lane = lane_id(), w = wave_id();
+    const int lg = lane >> 4, lq = lane & 15;
+    const int64_t h = blockIdx.y, b = blockIdx.z;
+    const int64_t gk = h / (g.Hq / g.Hkv);
+    const int64_t q0 = static_cast<int64_t>(blockIdx.x) * BQ, qw = q0 + WQ * w;
+    const int64_t shift = g.Lk - g.Lq;                 // causal: key j <= query i + shift
+    const float sl2 = g.scale * 1.4426950408889634f;    // scores in base 2
+    const uint16_t* Kb = g.K + (b * g.Hkv + gk) * g.Lk * D;
+    const uint16_t* Vb = g.V + (b * g.Hkv + gk) * g.Lk * D;
+
+    // Keys this workgroup visits: up to the last allowed key of its last query row.
+    const int64_t q_last = min<int64_t>(q0 + BQ, g.Lq) - 1;
+    int64_t kend = g.Lk;
+    if (g.causal) kend = max<int64_t>(0, min<int64_t>(g.Lk, q_last + shift + 1));
+    const int nblk = static_cast<int>((kend + BKV - 1) / BKV);
+
+    // Q fragments (second operand of S^T): query qw + 16 qt + lq, head-dim 32 kk + 8 lg .. + 7.
+    bf16x8 qf[2][KS];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int64_t qi = qw + 16 * qt + lq;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (qi < g.Lq) v = *reinterpret_cast<const u32x4*>(g.Q + ((b * g.Hq + h) * g.Lq + qi) * D + 32 * kk + 8 * lg);
+            qf[qt][kk] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    // Direct-to-LDS loads of key block j into buffer `buf` (rows past Lk read zeros).
+    const int lrow = lane / CPR, lchunk = lane % CPR;
+    auto load_block = [&](int j, int buf) {
+        const int64_t kv0 = static_cast<int64_t>(j) * BKV;
+        const int64_t rows = min<int64_t>(BKV, g.Lk - kv0);
+        const uint32_t bytes = static_cast<uint32_t>(rows * ROWB);
+        const auto rk = make_rsrc(Kb + kv0 * D, bytes), rv = make_rsrc(Vb + kv0 * D, bytes);
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int r = (4 * i + w) * RPI + lrow;   // row of this lane (< BKV)
+            const uint32_t ok = static_cast<uint32_t>(r * ROWB);
+            load_lds_16(rk, &lds[buf][0][(4 * i + w) * 1024], ok + 16u * static_cast<uint32_t>(lchunk ^ (r & 7)), 0u);
+            load_lds_16(rv, &lds[buf][1][(4 * i + w) * 1024], ok + 16u * static_cast<uint32_t>(lchunk ^ (2 * (r & 3))), 0u);
+        }
+    };
+
+    f32x4 oacc[DT][2];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) oacc[i][0] = oacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+    if (nblk > 0) load_block(0, 0);
+    for (int j = 0; j < nblk; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < nblk) {
+            load_block(j + 1, buf ^ 1);
+            wait_vmcnt<2 * LPT>();   // block j's loads (this wave) have landed
+        } else {
+            wait_vmcnt<0>();
+        }
+        barrier();                   // ... and every wave's
+        const uint8_t* Kt = lds[buf][0];
+        const uint8_t* Vt = lds[buf][1];
+        const int64_t kv0 = static_cast<int64_t>(j) * BKV;
+
+        // S^T = K Q^T: 4 key tiles x 2 query tiles.
+        f32x4 s[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[t][0] = s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = 16 * t + lq;
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kt + r * ROWB + 16 * ((4 * kk + lg) ^ (r & 7)));
+                s[t][0] = mfma_16x16x32(kf, qf[0][kk], s[t][0]);
+                s[t][1] = mfma_16x16x32(kf, qf[1][kk], s[t][1]);
+            }
+        }
+
+        // Online softmax per query (lane's query: qw + 16 qt + lq; keys kv0 + 16 t + 4 lg + r).
+        const bool edge = kv0 + BKV > g.Lk || (g.causal && kv0 + BKV - 1 > qw + shift);
+        u32x2 pb[2][4];   // P in bf16: [query tile][key tile], 4 keys each
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            const int64_t qi = qw + 16 * qt + lq;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = s[t][qt][r] * sl2;
+                    if (edge) {
+                        const int64_t kj = kv0 + 16 * t + 4 * lg + r;
+                        if (kj >= g.Lk || (g.causal && kj > qi + shift)) v = -INFINITY;
+                    }
+                    s[t][qt][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m[qt], mx);
+            const float alpha = m[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[qt] - mn);
+            float sum = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float p[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    p[r] = s[t][qt][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[t][qt][r] - mn);
+                    sum += p[r];
+                }
+                pb[qt][t] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+            }
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            l[qt] = l[qt] * alpha + sum;
+            m[qt] = mn;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oacc[dt][qt][r] *= alpha;
+        }
+
+        // O^T += V^T P^T over two 32-key steps (key tiles 2 st, 2 st + 1).
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            bf16x8 pf[2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
+                pf[qt] = __builtin_bit_cast(bf16x8, u32x4{pb[qt][2 * st][0], pb[qt][2 * st][1], pb[qt][2 * st + 1][0],
+                                                          pb[qt][2 * st + 1][1]});
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                u32x2 hv[2];
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                    // rows 16 (2 st + e2) + lane / 4, columns 16 dt + 4 (lane mod 4) .. + 3
+                    const int r = 16 * (2 * st + e2) + lane / 4;
+                    const int c = 2 * dt + ((lane & 3) >> 1);
+                    const int off = r * ROWB + 16 * (c ^ (2 * (r & 3))) + 8 * (lane & 1);
+                    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(Vt + off)));
+                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hv[e2]) : "v"(addr) : "memory");
+                }
+                // The transposing reads are assembly, whose results LLVM takes as ready at once:
+                // wait for them here, fenced so that no use is scheduled above the wait.
+                __builtin_amdgcn_sched_barrier(0);
+                wait_cnt<63, 0>();
+                __builtin_amdgcn_sched_barrier(0);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3));
+                oacc[dt][0] = mfma_16x16x32(vf, pf[0], oacc[dt][0]);
+                oacc[dt][1] = mfma_16x16x32(vf, pf[1], oacc[dt][1]);
+            }
+        }
+        barrier();   // every wave is done with buffer `buf` before block j + 2 is loaded into it
+    }
+
+    // O = O^T / l: lane holds query qw + 16 qt + lq, head-dim 16 dt + 4 lg .. + 3.
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int64_t qi = qw + 16 * qt + lq;
+        if (qi >= g.Lq) continue;
+        const float inv = l[qt] > 0.f ? 1.f / l[qt] : 0.f;
+        const int64_t orow = ((b * g.Hq + h) * g.Lq + qi) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 v = {oacc[dt][qt][0] * inv, oacc[dt][qt][1] * inv, oacc[dt][qt][2] * inv, oacc[dt][qt][3] * inv};
+            const int64_t c = 16 * dt + 4 * lg;
+            if constexpr (OUT == OUT_F32)
+                *reinterpret_cast<f32x4*>(static_cast<float*>(g.O) + orow + c) = v;
+            else
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.O) + orow + c) =
+                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+        if (g.LSE && lg == 0)
+            g.LSE[(b * g.Hq + h) * g.Lq + qi] = l[qt] > 0.f ? (m[qt] + log2f(l[qt])) * 0.6931471805599453f : -INFINITY;
+    }
+}
+
 hipError_t launch_attention(const AttnArgs& g, int out, const Plan& p, hipStream_t s) {
     const dim3 grid(p.grid_x, p.grid_y, p.grid_z);
-    if (out == OUT_F32)
+    if (p.kernel == K_ATTN_MFMA) {
+        if (g.d == 128 && out == OUT_F32)
+            hipLaunchKernelGGL((attn_mfma_kernel<128, OUT_F32>), grid, dim3(256), 0, s, g);
+        else if (g.d == 128)
+            hipLaunchKernelGGL((attn_mfma_kernel<128, OUT_BF16>), grid, dim3(256), 0, s, g);
+        else if (out == OUT_F32)
+            hipLaunchKernelGGL((attn_mfma_kernel<64, OUT_F32>), grid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((attn_mfma_kernel<64, OUT_BF16>), grid, dim3(256), 0, s, g);
+    } else if (out == OUT_F32) {
         hipLaunchKernelGGL(attn_simple_kernel<OUT_F32>, grid, dim3(256), 0, s, g);
-    else
+    } else {
         hipLaunchKernelGGL(attn_simple_kernel<OUT_BF16>, grid, dim3(256), 0, s, g);
+    }
     return hipGetLastError();
 }
 

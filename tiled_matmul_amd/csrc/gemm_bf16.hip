@@ -525,9 +525,12 @@ int validate_attn(const AttnShape& s) {
     return GEMM_OK;
 }
 
+// The MFMA kernel: head dimension 64 or 128; Q, K, V, O 16-byte aligned (16-byte loads of
+// Q rows and of K and V rows into LDS, vector stores of O).
 bool attn_mfma_ok(const AttnShape& s) {
-    (void)s;
-    return false;   // the MFMA kernel is not built yet
+    if (s.d != 64 && s.d != 128) return false;
+    if (!aligned(s.Q, 16) || !aligned(s.K, 16) || !aligned(s.V, 16) || !aligned(s.O, 16)) return false;
+    return s.Lk * s.d * 2 < k2G && cdiv(s.Lq, 128) < k2G;
 }
 
 int plan_attn(int variant, const AttnShape& s, int cus, Plan& p) {
@@ -542,7 +545,11 @@ int plan_attn(int variant, const AttnShape& s, int cus, Plan& p) {
     if (variant == ATTN_VARIANT_MFMA && !mfma) return GEMM_ERR_UNSUPPORTED;
     if (mfma && variant != ATTN_VARIANT_SIMPLE) {
         p.kernel = K_ATTN_MFMA;
-        return GEMM_ERR_UNSUPPORTED;
+        p.grid_x = static_cast<int>(cdiv(s.Lq, 128));
+        p.grid_y = static_cast<int>(s.Hq);
+        p.grid_z = static_cast<int>(s.B);
+        p.block = 256;
+        return GEMM_OK;
     }
     p.kernel = K_ATTN_SIMPLE;
     p.grid_x = static_cast<int>(cdiv(s.Lq, 4));
