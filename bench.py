@@ -228,6 +228,52 @@ def mx_leg(args, torch):
     }
 
 
+def attention_leg(args, torch):
+    """The attention forward (attention_fwd) on an attention workload, rotating input sets."""
+    name = args.workload
+    w = synth.ATTN_WORKLOADS[name]
+    B, Hq, Hkv, Lq, Lk, d, causal, out = (w[k] for k in ("B", "Hq", "Hkv", "Lq", "Lk", "d", "causal", "out"))
+    log(f"[bench] generating {name} inputs")
+    Q, K, V = synth.make_attention_inputs(name)
+    per = (Q.size + K.size + V.size) * 2 + Q.size * (4 if out == tm.GEMM_OUT_FP32 else 2)
+    nsets = max(1, -(-(args.rotate_mb * 2 ** 20) // per))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    base = [dev(Q), dev(K), dev(V)]
+    out_t = torch.float32 if out == tm.GEMM_OUT_FP32 else torch.bfloat16
+    sets = [[t if i == 0 else t.clone() for t in base] + [torch.empty(Q.shape, dtype=out_t, device="cuda")]
+            for i in range(nsets)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    q, k, v, o = sets[0]
+    rc, kname, grid, block = tm.attention_fwd_plan(0, B, Hq, Hkv, Lq, Lk, d, q, k, v, o, w["scale"],
+                                                   causal, out, cus)
+    if rc != 0:
+        raise SystemExit(f"attention_fwd cannot run {name}: {tm.gemm_bf16_status_string(rc)}")
+
+    def launch(i):
+        q, k, v, o = sets[i]
+        tm.attention_fwd(B, Hq, Hkv, Lq, Lk, d, q, k, v, o, None, w["scale"], causal, out)
+
+    log(f"[bench] timing {name}: kernel {kname}, {nsets} rotating buffer sets")
+    ms, wall = time_steps(launch, nsets, args.steps, args.warmup, torch)
+    # FLOPs of the two products over the (query, key) pairs the mask allows
+    pairs = sum(min(Lk, max(0, i + (Lk - Lq) + 1)) for i in range(Lq)) if causal else Lq * Lk
+    flops = 4.0 * B * Hq * pairs * d
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "attention forward TFLOP/s (bf16 MFMA, fp32 softmax and accumulation)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: B={B} Hq={Hq} Hkv={Hkv} Lq={Lq} Lk={Lk} d={d} "
+                               f"{'causal' if causal else 'full'}, {'fp32' if out == 0 else 'bf16'} out",
+                   "kernel": kname, "grid": grid, "block": block, "rotating_buffer_sets": nsets},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_TFLOPS, "traffic": traffic_for(kname, name),
+                     "flops_per_launch": flops},
+        "kernel_source_sha": kernel_source_sha(),
+    }
+
+
 def gemm_roofline(res):
     """The roof that binds this workload (by its arithmetic intensity against the ridge) and
     the achieved rate against it."""
@@ -355,7 +401,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square_4096",
-                    choices=sorted(synth.WORKLOADS) + sorted(synth.MX_WORKLOADS))
+                    choices=sorted(synth.WORKLOADS) + sorted(synth.MX_WORKLOADS)
+                    + sorted(synth.ATTN_WORKLOADS))
     ap.add_argument("--variant", default="auto", choices=sorted(tm.VARIANTS))
     ap.add_argument("--a-layout", default="k", choices=["k", "mn"],
                     help="A stored M x K (k) or K x M (mn)")
@@ -398,6 +445,9 @@ def main():
                           "kernel_source_sha": kernel_source_sha()}))
         return
 
+    if args.workload in synth.ATTN_WORKLOADS:
+        print(json.dumps(attention_leg(args, torch)))
+        return
     if args.workload in synth.MX_WORKLOADS:
         print(json.dumps(mx_leg(args, torch)))
         return

@@ -25,8 +25,10 @@
 //     follows the same order: two ds_read_b64_tr_b16 per fragment, each giving a lane 4
 //     consecutive keys of one head-dim column (the transposing read's lane layout: within 16
 //     lanes, lane i element e is element i mod 4 of the 8 bytes addressed by lane 4 e + i / 4).
-//   O^T accumulates in registers, rescaled by exp(m_old - m_new) per query before the block's
-//     products; each lane ends with 4 consecutive head-dim values of one query (vector stores).
+//   O^T accumulates in registers; each lane ends with 4 consecutive head-dim values of one
+//     query (vector stores).  Rescaling is selective: the reference maximum m of a query moves
+//     (and O^T and the sum are multiplied by exp(m_old - m_new)) only when a new score exceeds
+//     it by more than a factor 2^8, so most blocks skip the rescale.
 // LDS rows are d * 2 bytes; 16-byte chunk c of K row r sits at c ^ (r mod 8) (the K fragment
 // reads, 16 rows of one chunk, hit distinct banks) and chunk c of V row r at c ^ 2 (r mod 4)
 // (a transposing read touches 16 rows, 32 bytes each: 4 rows per 128-byte bank row).
@@ -121,6 +123,23 @@ namespace at {
 constexpr int BQ = 128, WQ = 32, BKV = 64;
 }
 
+// Max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that hold one query's
+// scores) with gfx950's row swaps, in the VALU: permlane16_swap(x, x) leaves rows (0, 0, 2, 2)
+// in one result and (1, 1, 3, 3) in the other, permlane32_swap(x, x) the low and the high
+// half; every lane combines the two in the same order, so the four copies agree bitwise.
+__device__ __forceinline__ float group4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D, int OUT>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
     using namespace at;
@@ -137,7 +156,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
     const int lg = lane >> 4, lq = lane & 15;
     const int64_t h = blockIdx.y, b = blockIdx.z;
     const int64_t gk = h / (g.Hq / g.Hkv);
-    const int64_t q0 = static_cast<int64_t>(blockIdx.x) * BQ, qw = q0 + WQ * w;
+    // Causal rows near the end see the most keys: start those workgroups first.
+    const int64_t qb = g.causal ? static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x : blockIdx.x;
+    const int64_t q0 = qb * BQ, qw = q0 + WQ * w;
     const int64_t shift = g.Lk - g.Lq;                 // causal: key j <= query i + shift
     const float sl2 = g.scale * 1.4426950408889634f;    // scores in base 2
     const uint16_t* Kb = g.K + (b * g.Hkv + gk) * g.Lk * D;
@@ -231,10 +252,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
                     s[t][qt][r] = v;
                     mx = fmaxf(mx, v);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mn = fmaxf(m[qt], mx);
-            const float alpha = m[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[qt] - mn);
+            mx = group4_max(mx);
+            // Selective rescaling: the reference maximum moves only when a score exceeds it by
+            // more than 2^8 (so probabilities stay <= 256, exact in fp32 sums and bf16's range);
+            // otherwise alpha is 1 and the output accumulators are left as they are.
+            const bool need = m[qt] == -INFINITY || mx > m[qt] + 8.f;
+            const float mn = need ? mx : m[qt];
+            const float alpha = !need ? 1.f : (m[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[qt] - mn));
             float sum = 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -246,14 +270,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
                 }
                 pb[qt][t] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
             }
-            sum += __shfl_xor(sum, 16, 64);
-            sum += __shfl_xor(sum, 32, 64);
+            sum = group4_sum(sum);
             l[qt] = l[qt] * alpha + sum;
             m[qt] = mn;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {   // wave-uniform
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+                for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) oacc[dt][qt][r] *= alpha;
+                    for (int r = 0; r < 4; ++r) oacc[dt][qt][r] *= alpha;
+            }
         }
 
         // O^T += V^T P^T over two 32-key steps (key tiles 2 st, 2 st + 1).
@@ -264,9 +289,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
             for (int qt = 0; qt < 2; ++qt)
                 pf[qt] = __builtin_bit_cast(bf16x8, u32x4{pb[qt][2 * st][0], pb[qt][2 * st][1], pb[qt][2 * st + 1][0],
                                                           pb[qt][2 * st + 1][1]});
+            // every V^T fragment of the step first (2 reads each), one wait, then the MFMAs
+            u32x2 hv[DT][2];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                u32x2 hv[2];
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int e2 = 0; e2 < 2; ++e2) {
                     // rows 16 (2 st + e2) + lane / 4, columns 16 dt + 4 (lane mod 4) .. + 3
@@ -274,14 +300,16 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
                     const int c = 2 * dt + ((lane & 3) >> 1);
                     const int off = r * ROWB + 16 * (c ^ (2 * (r & 3))) + 8 * (lane & 1);
                     const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(Vt + off)));
-                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hv[e2]) : "v"(addr) : "memory");
+                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hv[dt][e2]) : "v"(addr) : "memory");
                 }
-                // The transposing reads are assembly, whose results LLVM takes as ready at once:
-                // wait for them here, fenced so that no use is scheduled above the wait.
-                __builtin_amdgcn_sched_barrier(0);
-                wait_cnt<63, 0>();
-                __builtin_amdgcn_sched_barrier(0);
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3));
+            // The transposing reads are assembly, whose results LLVM takes as ready at once:
+            // wait for them here, fenced so that no use is scheduled above the wait.
+            __builtin_amdgcn_sched_barrier(0);
+            wait_cnt<63, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[dt][0], hv[dt][1], 0, 1, 2, 3));
                 oacc[dt][0] = mfma_16x16x32(vf, pf[0], oacc[dt][0]);
                 oacc[dt][1] = mfma_16x16x32(vf, pf[1], oacc[dt][1]);
             }
