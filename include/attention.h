@@ -34,7 +34,7 @@ extern "C" {
 #define ATTN_VARIANT_SIMPLE 1  /* one wave per query row, 64 keys per step (any d <= 256,
                                   d % 8 == 0)                                                */
 #define ATTN_VARIANT_MFMA 2    /* MFMA tiles of queries x keys, online softmax in registers
-                                  (d = 64 or 128; Q, K, V 16-byte aligned)                   */
+                                  (d = 64 or 128; scale > 0; Q, K, V, O 16-byte aligned)     */
 
 /*
  * The attention forward above.

@@ -234,38 +234,43 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
         }
 
         // Online softmax per query (lane's query: qw + 16 qt + lq; keys kv0 + 16 t + 4 lg + r).
+        // scale > 0 (planner), so the maximum is taken over the raw scores and scaled once, and
+        // each probability is one FMA and one exp2: exp2(s sl2 - m); masked scores are -inf,
+        // for which exp2 gives 0 (an all-masked row uses 0 as its reference instead of -inf).
         const bool edge = kv0 + BKV > g.Lk || (g.causal && kv0 + BKV - 1 > qw + shift);
         u32x2 pb[2][4];   // P in bf16: [query tile][key tile], 4 keys each
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-            const int64_t qi = qw + 16 * qt + lq;
+            if (edge) {
+                const int64_t qi = qw + 16 * qt + lq;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t kj = kv0 + 16 * t + 4 * lg + r;
+                        if (kj >= g.Lk || (g.causal && kj > qi + shift)) s[t][qt][r] = -INFINITY;
+                    }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = s[t][qt][r] * sl2;
-                    if (edge) {
-                        const int64_t kj = kv0 + 16 * t + 4 * lg + r;
-                        if (kj >= g.Lk || (g.causal && kj > qi + shift)) v = -INFINITY;
-                    }
-                    s[t][qt][r] = v;
-                    mx = fmaxf(mx, v);
-                }
-            mx = group4_max(mx);
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[t][qt][r]);
+            mx = group4_max(mx) * sl2;
             // Selective rescaling: the reference maximum moves only when a score exceeds it by
-            // more than 2^8 (so probabilities stay <= 256, exact in fp32 sums and bf16's range);
-            // otherwise alpha is 1 and the output accumulators are left as they are.
+            // more than 2^8 (so probabilities stay <= 256, exact in fp32 sums and within bf16's
+            // range); otherwise alpha is 1 and the accumulators are left as they are.
             const bool need = m[qt] == -INFINITY || mx > m[qt] + 8.f;
             const float mn = need ? mx : m[qt];
             const float alpha = !need ? 1.f : (m[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[qt] - mn));
+            const float nref = mn == -INFINITY ? 0.f : -mn;
             float sum = 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 float p[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    p[r] = s[t][qt][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[t][qt][r] - mn);
+                    p[r] = __builtin_amdgcn_exp2f(fmaf(s[t][qt][r], sl2, nref));
                     sum += p[r];
                 }
                 pb[qt][t] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};

@@ -529,6 +529,7 @@ int validate_attn(const AttnShape& s) {
 // Q rows and of K and V rows into LDS, vector stores of O).
 bool attn_mfma_ok(const AttnShape& s) {
     if (s.d != 64 && s.d != 128) return false;
+    if (!(s.scale > 0.f)) return false;   // the kernel scales the row maximum once
     if (!aligned(s.Q, 16) || !aligned(s.K, 16) || !aligned(s.V, 16) || !aligned(s.O, 16)) return false;
     return s.Lk * s.d * 2 < k2G && cdiv(s.Lq, 128) < k2G;
 }
