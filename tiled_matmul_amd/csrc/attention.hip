@@ -218,20 +218,27 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
         const uint8_t* Vt = lds[buf][1];
         const int64_t kv0 = static_cast<int64_t>(j) * BKV;
 
-        // S^T = K Q^T: 4 key tiles x 2 query tiles.
+        // S^T = K Q^T: 4 key tiles x 2 query tiles.  Every K fragment of the block is read
+        // first, then the MFMAs run in the same order, each waiting only for its own read.
         f32x4 s[4][2];
 #pragma unroll
         for (int t = 0; t < 4; ++t) s[t][0] = s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 kf[KS][4];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
+        for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int r = 16 * t + lq;
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kt + r * ROWB + 16 * ((4 * kk + lg) ^ (r & 7)));
-                s[t][0] = mfma_16x16x32(kf, qf[0][kk], s[t][0]);
-                s[t][1] = mfma_16x16x32(kf, qf[1][kk], s[t][1]);
+                kf[kk][t] = *reinterpret_cast<const bf16x8*>(Kt + r * ROWB + 16 * ((4 * kk + lg) ^ (r & 7)));
             }
-        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                s[t][0] = mfma_16x16x32(kf[kk][t], qf[0][kk], s[t][0]);
+                s[t][1] = mfma_16x16x32(kf[kk][t], qf[1][kk], s[t][1]);
+            }
 
         // Online softmax per query (lane's query: qw + 16 qt + lq; keys kv0 + 16 t + 4 lg + r).
         // scale > 0 (planner), so the maximum is taken over the raw scores and scaled once, and
@@ -286,16 +293,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
             }
         }
 
-        // O^T += V^T P^T over two 32-key steps (key tiles 2 st, 2 st + 1).
+        // O^T += V^T P^T over two 32-key steps (key tiles 2 st, 2 st + 1).  The V^T fragments
+        // of both steps are read first (two transposing reads each); the first step's MFMAs
+        // wait only for the first step's reads, so the second step's reads overlap them.
+        u32x2 hv[2][DT][2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            bf16x8 pf[2];
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-                pf[qt] = __builtin_bit_cast(bf16x8, u32x4{pb[qt][2 * st][0], pb[qt][2 * st][1], pb[qt][2 * st + 1][0],
-                                                          pb[qt][2 * st + 1][1]});
-            // every V^T fragment of the step first (2 reads each), one wait, then the MFMAs
-            u32x2 hv[DT][2];
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -305,16 +308,28 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
                     const int c = 2 * dt + ((lane & 3) >> 1);
                     const int off = r * ROWB + 16 * (c ^ (2 * (r & 3))) + 8 * (lane & 1);
                     const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(Vt + off)));
-                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hv[dt][e2]) : "v"(addr) : "memory");
+                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hv[st][dt][e2]) : "v"(addr) : "memory");
                 }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            bf16x8 pf[2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
+                pf[qt] = __builtin_bit_cast(bf16x8, u32x4{pb[qt][2 * st][0], pb[qt][2 * st][1], pb[qt][2 * st + 1][0],
+                                                          pb[qt][2 * st + 1][1]});
             // The transposing reads are assembly, whose results LLVM takes as ready at once:
-            // wait for them here, fenced so that no use is scheduled above the wait.
+            // wait for them here, fenced so that no use is scheduled above the wait.  LDS
+            // reads complete in order; at most 2 DT - 1 <= 15 of the second step's reads may
+            // still be outstanding once the first step's have landed.
             __builtin_amdgcn_sched_barrier(0);
-            wait_cnt<63, 0>();
+            if (st == 0)
+                wait_cnt<63, 2 * DT - 1>();
+            else
+                wait_cnt<63, 0>();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[dt][0], hv[dt][1], 0, 1, 2, 3));
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[st][dt][0], hv[st][dt][1], 0, 1, 2, 3));
                 oacc[dt][0] = mfma_16x16x32(vf, pf[0], oacc[dt][0]);
                 oacc[dt][1] = mfma_16x16x32(vf, pf[1], oacc[dt][1]);
             }

@@ -80,8 +80,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
+// Two values in one v_cvt_pk_bf16_f32 (lo in bits 0-15), rounded as f32_to_bf16 rounds.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
