@@ -29,9 +29,8 @@
 //     query (vector stores).  Rescaling is selective: the reference maximum m of a query moves
 //     (and O^T and the sum are multiplied by exp(m_old - m_new)) only when a new score exceeds
 //     it by more than a factor 2^8, so most blocks skip the rescale.
-// LDS rows are d * 2 bytes; 16-byte chunk c of K row r sits at c ^ (r mod 8) (the K fragment
-// reads, 16 rows of one chunk, hit distinct banks) and chunk c of V row r at c ^ 2 (r mod 4)
-// (a transposing read touches 16 rows, 32 bytes each: 4 rows per 128-byte bank row).
+// LDS rows are d * 2 bytes, their 16-byte chunks permuted by an XOR swizzle per row so that
+// the K fragment reads and the transposing V reads are free of bank conflicts.
 // Scores and the exponent are in base 2 (scale log2(e) folded into the scores).
 #include <math.h>
 
@@ -151,6 +150,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
     constexpr int KS = D / 32;             // k steps of S^T
     constexpr int DT = D / 16;             // 16-wide head-dim tiles of O^T
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][TILE];   // [buffer][K, V]
+    // LDS position of 16-byte chunk c of K row r: c ^ kswz(r); of V row r: c ^ vswz(r).  The
+    // LDS has 64 banks of 4 bytes (a 256-byte bank row, RP rows of a tile).  A K fragment read
+    // (16 rows, one chunk each) then meets 16 different chunk positions at d = 128 and 8
+    // positions in each of the two row halves at d = 64; a transposing V read (8 rows of 32
+    // bytes per 256 bytes delivered) meets 8 different 32-byte positions of a bank row.  Both
+    // are free of bank conflicts (measured: SQ_LDS_BANK_CONFLICT 0).
+    constexpr int RP = 256 / ROWB;
+    auto kswz = [](int r) { return r & (CPR - 1); };
+    auto vswz = [](int r) { return 2 * ((r / RP) & (CPR / 2 - 1)); };
 
     const int lane = lane_id(), w = wave_id();
     const int lg = lane >> 4, lq = lane & 15;
@@ -194,8 +202,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
         for (int i = 0; i < LPT; ++i) {
             const int r = (4 * i + w) * RPI + lrow;   // row of this lane (< BKV)
             const uint32_t ok = static_cast<uint32_t>(r * ROWB);
-            load_lds_16(rk, &lds[buf][0][(4 * i + w) * 1024], ok + 16u * static_cast<uint32_t>(lchunk ^ (r & 7)), 0u);
-            load_lds_16(rv, &lds[buf][1][(4 * i + w) * 1024], ok + 16u * static_cast<uint32_t>(lchunk ^ (2 * (r & 3))), 0u);
+            load_lds_16(rk, &lds[buf][0][(4 * i + w) * 1024], ok + 16u * static_cast<uint32_t>(lchunk ^ kswz(r)), 0u);
+            load_lds_16(rv, &lds[buf][1][(4 * i + w) * 1024], ok + 16u * static_cast<uint32_t>(lchunk ^ vswz(r)), 0u);
         }
     };
 
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int r = 16 * t + lq;
-                kf[kk][t] = *reinterpret_cast<const bf16x8*>(Kt + r * ROWB + 16 * ((4 * kk + lg) ^ (r & 7)));
+                kf[kk][t] = *reinterpret_cast<const bf16x8*>(Kt + r * ROWB + 16 * ((4 * kk + lg) ^ kswz(r)));
             }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
                     // rows 16 (2 st + e2) + lane / 4, columns 16 dt + 4 (lane mod 4) .. + 3
                     const int r = 16 * (2 * st + e2) + lane / 4;
                     const int c = 2 * dt + ((lane & 3) >> 1);
-                    const int off = r * ROWB + 16 * (c ^ (2 * (r & 3))) + 8 * (lane & 1);
+                    const int off = r * ROWB + 16 * (c ^ vswz(r)) + 8 * (lane & 1);
                     const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(Vt + off)));
                     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hv[st][dt][e2]) : "v"(addr) : "memory");
                 }
