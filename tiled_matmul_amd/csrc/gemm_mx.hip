@@ -8,9 +8,9 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 computes natively.
 //
 // mx_ring_kernel is the 4-wave ring kernel of gemm_ring.hip with bytes for elements: a
-// 256 x 128-byte LDS row holds 128 k, so the ring geometry (A: 3 slots, B: 2 slots of 32 KB),
-// the swizzle and the direct-to-LDS loads are unchanged; a 128-deep block is two 64-deep k
-// steps of 32 x 32 x 64 MFMAs.  Operand layout of that MFMA, measured on MI355X with an
+// 256 x 128-byte LDS row holds 128 k, so the ring geometry (A: 3 slots, B: 2 slots of 32 KB)
+// and the direct-to-LDS loads are unchanged (the swizzle differs: a fragment read here spans
+// 32 rows, not 16); a 128-deep block is two 64-deep k steps of 32 x 32 x 64 MFMAs.  Operand layout of that MFMA, measured on MI355X with an
 // in-bounds probe: lane l supplies row l % 32; with g = l / 32, bytes 0-15 of its 32 are
 // k = 16 g .. 16 g + 15 and bytes 16-31 are k = 32 + 16 g .. 32 + 16 g + 15 of the 64-deep
 // step, and the scale operand of lane group h applies to k = 32 h .. 32 h + 31.  So a lane
@@ -39,7 +39,11 @@ constexpr int TILE = 256 * ROWB;
 constexpr int B_BASE = NA * TILE;
 constexpr int R = 8;   // LDS rows per wave load instruction
 static_assert((NA + NB) * TILE <= 160 * 1024, "LDS capacity");
-__device__ __forceinline__ int swz(int r) { return r & 7; }
+// LDS position of 16-byte chunk c of tile row r: c ^ swz(r).  A fragment read takes one chunk
+// of 32 consecutive rows (two rows per 256-byte bank row); swz sends the rows that share a
+// bank position to lanes 8, 34 or 42 apart, which the LDS serves without a conflict
+// (measured: SQ_LDS_BANK_CONFLICT 0).  swz depends on bits 1, 2 and 4 of r only.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
 }  // namespace mx
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
@@ -98,7 +102,8 @@ __global__ __launch_bounds__(256, 1) void mx_ring_kernel(MxArgs g, TileGrid tg, 
     const int nk = static_cast<int>(g.K / BKB);
     const int lg = lane >> 5;                 // lane group: 32-block 2 kk + lg of a k step
     const int lrow = lane / 8;
-    const uint32_t chunk_b = 16u * static_cast<uint32_t>((lane % 8) ^ swz(lrow));
+    // Every load of this lane writes a tile row congruent to 8 w + lrow modulo 32.
+    const uint32_t chunk_b = 16u * static_cast<uint32_t>((lane % 8) ^ swz(8 * w + lrow));
     // Fragment read e (0, 1) of k step kk: row lane % 32 of the fragment, chunk 4 kk + 2 e + lg.
     int rd[2][2];
 #pragma unroll

@@ -63,13 +63,15 @@ __device__ __forceinline__ int swz(int r) { return r & 7; }
 // 32: v_mfma_f32_32x32x16_bf16, two per k step).  AMN / BMN: the A / B operand is MN-major
 // (element (i, k) at k * ld + i; MF = 16 only).  An MN-major tile sits in LDS as 64 k-rows
 // of 256 elements (512 bytes), 16-byte chunk c of k-row r at chunk c ^ 2 sigma(r) with
-// sigma(r) = (r ^ (r >> 2)) mod 8; its fragments are read with ds_read_b64_tr_b16, which
+// sigma(r) = ((r >> 3) mod 4) ^ 2 (r mod 4) ^ ((r >> 2) mod 2) (bits 0-4 of r only); its
+// fragments are read with ds_read_b64_tr_b16, which
 // within each group of 16 lanes returns to lane i, element e, element (i mod 4) of the
 // 8 bytes addressed by lane 4 e + i / 4 (measured on MI355X).  So lane j of group g
 // addresses k-row 8 g + 4 e2 + j / 4, columns 4 (j mod 4) .. + 3 of the fragment, and lane
 // i receives the 4 consecutive k of column i: two such reads (e2 = 0, 1) make the MFMA
-// operand.  Each transpose read of 64 lanes touches 16 k-rows; sigma spreads them over 8
-// positions of a 256-byte bank row.
+// operand.  Each transpose read of 64 lanes touches 16 k-rows, 8 per half-wave; sigma gives
+// the 8 k-rows of each half-wave 8 different 32-byte positions of a 256-byte bank row, so
+// the read is free of bank conflicts (measured: SQ_LDS_BANK_CONFLICT 0).
 // OUT: OUT_F32 or OUT_BF16 into C, or OUT_PARTIAL: split K, the fp32 partial sum of each work
 // item's K range into the workspace (its own instance, so that the other instances keep one
 // range per tile as a compile-time constant and their registers).
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
 
     // MN-major tiles.  Load i of wave w: k-rows (NW i + w) 2 + lane / 32, physical chunk
     // lane % 32, logical chunk (lane % 32) ^ 2 sigma(k-row).
-    auto sigma = [](int r) { return (r ^ (r >> 2)) & 7; };
+    auto sigma = [](int r) { return ((r >> 3) & 3) ^ ((r & 3) << 1) ^ ((r >> 2) & 1); };
     int mn_col[L];   // element column (within the tile) this lane fetches in load i
 #pragma unroll
     for (int i = 0; i < L; ++i) {
