@@ -121,7 +121,11 @@ def test_plan_variant_preconditions():
     assert plan(variant=9)[3] == 256
     assert plan(variant=9, K=4099, lda=4100, ldb=4100)[:2] == (0, "ring4_256")
     assert plan(variant=9, A=P + 2)[0] == tm.GEMM_ERR_UNSUPPORTED
-    assert plan(variant=10)[0] == tm.GEMM_ERR_ARG
+    assert plan(variant=10)[:2] == (0, "dtv_256")
+    assert plan(variant=10)[3] == 256
+    assert plan(variant=10, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED      # 16-byte chunks need K % 8 == 0
+    assert plan(variant=10, A=P + 8)[0] == tm.GEMM_ERR_UNSUPPORTED     # and 16-byte aligned rows
+    assert plan(variant=11)[0] == tm.GEMM_ERR_ARG
     assert plan(variant=1)[1] == "simple_64"
     assert plan(variant=2)[1] == "mfma_128"
 
@@ -182,9 +186,9 @@ def test_layout_plan():
     assert lplan(KM, MN, variant=1)[:2] == (0, "simple_64")
     assert lplan(KM, MN, variant=9)[:2] == (0, "ring4_256")
     assert lplan(KM, MN, variant=9, N=4093)[0] == tm.GEMM_ERR_UNSUPPORTED
-    for variant in (2, 3, 4, 5, 6, 7, 8):
+    for variant in (2, 3, 4, 5, 6, 7, 8, 10):
         assert lplan(KM, MN, variant=variant)[0] == tm.GEMM_ERR_UNSUPPORTED, variant
-    assert lplan(KM, MN, variant=10)[0] == tm.GEMM_ERR_ARG
+    assert lplan(KM, MN, variant=11)[0] == tm.GEMM_ERR_ARG
     # K = 0: zero fill in any layout
     assert lplan(MN, MN, K=0, lda=4096, ldb=4096)[:2] == (0, "zero_fill")
     # both K-major: the K-major planner (the GEMV path included)

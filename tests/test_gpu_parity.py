@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 V = tm
 ALL_TILED = [V.GEMM_VARIANT_SIMPLE, V.GEMM_VARIANT_MFMA, V.GEMM_VARIANT_PIPELINED,
              V.GEMM_VARIANT_PERSISTENT, V.GEMM_VARIANT_SPECIALIZED, V.GEMM_VARIANT_PINGPONG,
-             V.GEMM_VARIANT_RING8, V.GEMM_VARIANT_RING4, V.GEMM_VARIANT_AUTO]
+             V.GEMM_VARIANT_RING8, V.GEMM_VARIANT_RING4, V.GEMM_VARIANT_DTV, V.GEMM_VARIANT_AUTO]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -289,6 +289,39 @@ def test_workload_sampled_rows(name):
     assert np.isfinite(got).all()
     A, B, got = workload_run(name, integer=True)
     assert_exact(got[rows], A, B, K, out_dtype, rows=rows, what=name + " integer")
+
+
+# The kernel with A in registers: K not a multiple of the 64-deep block (the last block
+# partly past K) and an odd block count (the loop runs one block of zeros), rows of A and B
+# beyond M and N, padded pitches with NaN between rows.
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (300, 520, 72), (520, 300, 200), (257, 1000, 4104),
+                                   (1024, 768, 3000), (40, 24, 8)])
+def test_dtv_block_tails(M, N, K):
+    A = synth.integers(M, K, 401 + K, ld=K + 16)
+    B = synth.integers(N, K, 402 + K, ld=K + 8)
+    for out_dtype in (OUT_FP32, OUT_BF16):
+        got = run_gemm(A, B, K, out_dtype, variant=V.GEMM_VARIANT_DTV, ldc=N + 4)
+        assert_exact(got, A, B, K, out_dtype, what=f"dtv {M}x{N}x{K}")
+
+
+# The same kernel at the full sizes of the large workloads (sampled rows).
+@pytest.mark.parametrize("name", ["square_4096", "ffn_up_8192x14336x4096", "ffn_down_8192x4096x14336"])
+def test_dtv_workload_sampled_rows(name):
+    w = synth.WORKLOADS[name]
+    M, N, K, out_dtype = w["M"], w["N"], w["K"], w["out"]
+    rows = sample_rows(M)
+    for integer in (False, True):
+        if integer:
+            sa, sb = synth.seeds(w["cfg"])
+            A, B = synth.integers(M, K, sa), synth.integers(N, K, sb)
+        else:
+            A, B = synth.make_operands(name)
+        got = run_gemm(A, B, K, out_dtype, variant=V.GEMM_VARIANT_DTV)
+        if integer:
+            assert_exact(got[rows], A, B, K, out_dtype, rows=rows, what=name + " dtv integer")
+        else:
+            assert_bound(got[rows], A, B, K, out_dtype, rows=rows, what=name + " dtv")
+            assert np.isfinite(got).all()
 
 
 @pytest.mark.parametrize("out_dtype", [OUT_FP32, OUT_BF16])

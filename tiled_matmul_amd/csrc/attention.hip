@@ -119,8 +119,26 @@ __global__ __launch_bounds__(256) void attn_simple_kernel(AttnArgs g) {
 }
 
 namespace at {
-constexpr int BQ = 128, WQ = 32, BKV = 64;
+constexpr int BKV = 64;
 }
+
+// 16-query tiles per wave of attn_mfma_kernel at d = 128 and d = 64 (a workgroup of 4 waves
+// takes 64 QT queries).  QT = 2 runs two workgroups per CU; QT = 4 halves the LDS fragment
+// reads per MFMA (every K and V^T fragment a wave reads serves twice as many queries) with
+// one workgroup (one wave per SIMD, accumulators in AGPRs).
+#ifndef TMM_ATTN_QT128
+#define TMM_ATTN_QT128 2
+#endif
+#ifndef TMM_ATTN_QT64
+#define TMM_ATTN_QT64 2
+#endif
+
+// Wave priority raised over each block's two MFMA phases (1) or left alone (0).
+#ifndef TMM_ATTN_SETPRIO
+#define TMM_ATTN_SETPRIO 1
+#endif
+
+int attn_rows_per_workgroup(int d) { return 64 * (d == 128 ? TMM_ATTN_QT128 : TMM_ATTN_QT64); }
 
 // Max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that hold one query's
 // scores) with gfx950's row swaps, in the VALU: permlane16_swap(x, x) leaves rows (0, 0, 2, 2)
@@ -139,9 +157,10 @@ __device__ __forceinline__ float group4_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int OUT>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
+template <int D, int OUT, int QT>
+__global__ __launch_bounds__(256, QT == 2 ? 2 : 1) void attn_mfma_kernel(AttnArgs g) {
     using namespace at;
+    constexpr int WQ = 16 * QT, BQ = 4 * WQ;   // queries per wave, per workgroup
     constexpr int ROWB = D * 2;            // bytes per LDS row
     constexpr int CPR = D / 8;             // 16-byte chunks per row
     constexpr int TILE = BKV * ROWB;       // one K or V tile
@@ -179,9 +198,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
     const int nblk = static_cast<int>((kend + BKV - 1) / BKV);
 
     // Q fragments (second operand of S^T): query qw + 16 qt + lq, head-dim 32 kk + 8 lg .. + 7.
-    bf16x8 qf[2][KS];
+    bf16x8 qf[QT][KS];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
         const int64_t qi = qw + 16 * qt + lq;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
@@ -207,10 +226,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
         }
     };
 
-    f32x4 oacc[DT][2];
+    f32x4 oacc[DT][QT];
+    float m[QT], l[QT];
 #pragma unroll
-    for (int i = 0; i < DT; ++i) oacc[i][0] = oacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+        for (int i = 0; i < DT; ++i) oacc[i][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[qt] = -INFINITY, l[qt] = 0.f;
+    }
+    // Causal: key blocks that start past the last key this wave's last query may see add
+    // nothing to its rows; the wave skips their products and softmax (not the barriers).
+    const int64_t wave_kend = g.causal ? qw + WQ - 1 + shift : g.Lk - 1;
 
     if (nblk > 0) load_block(0, 0);
     for (int j = 0; j < nblk; ++j) {
@@ -225,12 +251,16 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
         const uint8_t* Kt = lds[buf][0];
         const uint8_t* Vt = lds[buf][1];
         const int64_t kv0 = static_cast<int64_t>(j) * BKV;
+        if (kv0 <= wave_kend) {   // wave-uniform
 
+        if (TMM_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
         // S^T = K Q^T: 4 key tiles x 2 query tiles.  Every K fragment of the block is read
         // first, then the MFMAs run in the same order, each waiting only for its own read.
-        f32x4 s[4][2];
+        f32x4 s[4][QT];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s[t][0] = s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) s[t][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
         bf16x8 kf[KS][4];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
@@ -243,19 +273,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                s[t][0] = mfma_16x16x32(kf[kk][t], qf[0][kk], s[t][0]);
-                s[t][1] = mfma_16x16x32(kf[kk][t], qf[1][kk], s[t][1]);
-            }
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) s[t][qt] = mfma_16x16x32(kf[kk][t], qf[qt][kk], s[t][qt]);
 
+        if (TMM_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         // Online softmax per query (lane's query: qw + 16 qt + lq; keys kv0 + 16 t + 4 lg + r).
         // scale > 0 (planner), so the maximum is taken over the raw scores and scaled once, and
         // each probability is one FMA and one exp2: exp2(s sl2 - m); masked scores are -inf,
         // for which exp2 gives 0 (an all-masked row uses 0 as its reference instead of -inf).
         const bool edge = kv0 + BKV > g.Lk || (g.causal && kv0 + BKV - 1 > qw + shift);
-        u32x2 pb[2][4];   // P in bf16: [query tile][key tile], 4 keys each
+        u32x2 pb[QT][4];   // P in bf16: [query tile][key tile], 4 keys each
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int qt = 0; qt < QT; ++qt) {
             if (edge) {
                 const int64_t qi = qw + 16 * qt + lq;
 #pragma unroll
@@ -301,6 +331,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
             }
         }
 
+        if (TMM_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
         // O^T += V^T P^T over two 32-key steps (key tiles 2 st, 2 st + 1).  The V^T fragments
         // of both steps are read first (two transposing reads each); the first step's MFMAs
         // wait only for the first step's reads, so the second step's reads overlap them.
@@ -320,9 +351,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
                 }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            bf16x8 pf[2];
+            bf16x8 pf[QT];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
+            for (int qt = 0; qt < QT; ++qt)
                 pf[qt] = __builtin_bit_cast(bf16x8, u32x4{pb[qt][2 * st][0], pb[qt][2 * st][1], pb[qt][2 * st + 1][0],
                                                           pb[qt][2 * st + 1][1]});
             // The transposing reads are assembly, whose results LLVM takes as ready at once:
@@ -338,16 +369,18 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[st][dt][0], hv[st][dt][1], 0, 1, 2, 3));
-                oacc[dt][0] = mfma_16x16x32(vf, pf[0], oacc[dt][0]);
-                oacc[dt][1] = mfma_16x16x32(vf, pf[1], oacc[dt][1]);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_16x16x32(vf, pf[qt], oacc[dt][qt]);
             }
         }
+        if (TMM_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        }          // kv0 <= wave_kend
         barrier();   // every wave is done with buffer `buf` before block j + 2 is loaded into it
     }
 
     // O = O^T / l: lane holds query qw + 16 qt + lq, head-dim 16 dt + 4 lg .. + 3.
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
         const int64_t qi = qw + 16 * qt + lq;
         if (qi >= g.Lq) continue;
         const float inv = l[qt] > 0.f ? 1.f / l[qt] : 0.f;
@@ -370,14 +403,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs g) {
 hipError_t launch_attention(const AttnArgs& g, int out, const Plan& p, hipStream_t s) {
     const dim3 grid(p.grid_x, p.grid_y, p.grid_z);
     if (p.kernel == K_ATTN_MFMA) {
+        constexpr int Q1 = TMM_ATTN_QT128, Q6 = TMM_ATTN_QT64;
         if (g.d == 128 && out == OUT_F32)
-            hipLaunchKernelGGL((attn_mfma_kernel<128, OUT_F32>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((attn_mfma_kernel<128, OUT_F32, Q1>), grid, dim3(256), 0, s, g);
         else if (g.d == 128)
-            hipLaunchKernelGGL((attn_mfma_kernel<128, OUT_BF16>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((attn_mfma_kernel<128, OUT_BF16, Q1>), grid, dim3(256), 0, s, g);
         else if (out == OUT_F32)
-            hipLaunchKernelGGL((attn_mfma_kernel<64, OUT_F32>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((attn_mfma_kernel<64, OUT_F32, Q6>), grid, dim3(256), 0, s, g);
         else
-            hipLaunchKernelGGL((attn_mfma_kernel<64, OUT_BF16>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((attn_mfma_kernel<64, OUT_BF16, Q6>), grid, dim3(256), 0, s, g);
     } else if (out == OUT_F32) {
         hipLaunchKernelGGL(attn_simple_kernel<OUT_F32>, grid, dim3(256), 0, s, g);
     } else {

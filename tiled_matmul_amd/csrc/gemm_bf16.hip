@@ -177,6 +177,20 @@ int plan_spec(const Shape& s, int cus, Plan& p, int kernel = K_SPEC_256) {
     return GEMM_OK;
 }
 
+// A in registers, B in an LDS ring: both operands K-major with 16-byte loads (the A
+// fragments are 16-byte buffer loads into registers), 256 x 256 tiles, persistent.
+int plan_dtv(const Shape& s, int cus, Plan& p) {
+    if (s.la != GEMM_LAYOUT_K_MAJOR || s.lb != GEMM_LAYOUT_K_MAJOR || !fast_loads_ok(s, 256))
+        return GEMM_ERR_UNSUPPORTED;
+    tile_grid(s, 256, 256, p);
+    p.kernel = K_DTV_256;
+    p.grid_x = std::min(p.grid.total, cus);
+    p.grid_y = p.grid_z = 1;
+    p.block = 256;
+    p.vec_store = vec_store_ok(s);
+    return GEMM_OK;
+}
+
 bool gemv_ok(const Shape& s) {
     if (s.M > 16 || s.batch != 1) return false;
     if (!aligned(s.A, 16) || !aligned(s.B, 16) || s.lda % 8 || s.ldb % 8 || s.K % 8) return false;
@@ -233,7 +247,7 @@ int plan_layout(int variant, const Shape& s, int cus, Plan& p) {
 }
 
 int make_plan(int variant, const Shape& s, int cus, Plan& p) {
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_RING4) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_DTV) return GEMM_ERR_ARG;
     p = Plan{};
     if (s.batch == 0 || s.M == 0 || s.N == 0) {
         p.kernel = K_NONE;
@@ -257,6 +271,7 @@ int make_plan(int variant, const Shape& s, int cus, Plan& p) {
         case GEMM_VARIANT_PINGPONG: return plan_spec(s, cus, p, K_PINGPONG_256);
         case GEMM_VARIANT_RING8: return plan_spec(s, cus, p, K_RING8_256);
         case GEMM_VARIANT_RING4: return plan_spec(s, cus, p, K_RING4_256);
+        case GEMM_VARIANT_DTV: return plan_dtv(s, cus, p);
         default: break;
     }
     // AUTO
@@ -272,7 +287,7 @@ int run(int variant, const Shape& s, void* stream) {
     int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
                       s.out);
     if (rc != GEMM_OK) return rc;
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_RING4) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_DTV) return GEMM_ERR_ARG;
     if (s.batch == 0 || s.M == 0 || s.N == 0) return GEMM_OK;
     int cus = 0;
     rc = current_device(&cus);
@@ -299,6 +314,7 @@ int run(int variant, const Shape& s, void* stream) {
         case K_PINGPONG_256: e = launch_pingpong(g, s.out, p, st); break;
         case K_RING8_256:
         case K_RING4_256: e = launch_ring(g, s.out, p, st); break;
+        case K_DTV_256: e = launch_dtv(g, s.out, p, st); break;
         case K_GEMV: e = launch_gemv(g, s.out, p, st); break;
         case K_GEMV_LDS: e = launch_gemv_lds(g, s.out, p, st); break;
         default: return GEMM_ERR_UNSUPPORTED;
@@ -389,7 +405,7 @@ int plan_into(int variant, const Shape& s, int num_cus, int* kernel_id, int64_t*
     int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
                       s.out);
     if (rc != GEMM_OK) return rc;
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_RING4) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_DTV) return GEMM_ERR_ARG;
     Plan p;
     rc = make_plan(variant, s, num_cus > 0 ? num_cus : kDefaultCUs, p);
     if (rc != GEMM_OK) return rc;
@@ -546,7 +562,7 @@ int plan_attn(int variant, const AttnShape& s, int cus, Plan& p) {
     if (variant == ATTN_VARIANT_MFMA && !mfma) return GEMM_ERR_UNSUPPORTED;
     if (mfma && variant != ATTN_VARIANT_SIMPLE) {
         p.kernel = K_ATTN_MFMA;
-        p.grid_x = static_cast<int>(cdiv(s.Lq, 128));
+        p.grid_x = static_cast<int>(cdiv(s.Lq, attn_rows_per_workgroup(static_cast<int>(s.d))));
         p.grid_y = static_cast<int>(s.Hq);
         p.grid_z = static_cast<int>(s.B);
         p.block = 256;
@@ -759,6 +775,7 @@ const char* gemm_bf16_kernel_name(int k) {
         case K_PINGPONG_256: return "pingpong_256";
         case K_RING8_256: return "ring8_256";
         case K_RING4_256: return "ring4_256";
+        case K_DTV_256: return "dtv_256";
         case K_MX_RING_256: return "mx_ring_256";
         case K_MX_SIMPLE_64: return "mx_simple_64";
         case K_ATTN_SIMPLE: return "attn_simple";

@@ -28,7 +28,8 @@ enum KernelId {
     K_MX_SIMPLE_64 = 15,    //   general fallback (any K multiple of 32, pitch, alignment)
     K_ATTN_SIMPLE = 16,     // attention forward: one wave per query row (any d <= 256)
     K_ATTN_MFMA = 17,       //   MFMA tiles of queries x keys, online softmax (d = 64, 128)
-    K_COUNT = 18
+    K_DTV_256 = 18,         // steps 4-6 with the A operand loaded straight into MFMA registers, B ring in LDS
+    K_COUNT = 19
 };
 
 // Launch shape chosen for a problem (filled by the planner, consumed by the launchers).
@@ -46,6 +47,7 @@ hipError_t launch_mfma(const GemmArgs& g, int out, const Plan& p, hipStream_t s)
 hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_pingpong(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_ring(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_dtv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs& g, int out, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_mx(const MxArgs& g, int out, const Plan& p, hipStream_t s);
@@ -53,5 +55,6 @@ hipError_t launch_attention(const AttnArgs& g, int out, const Plan& p, hipStream
 hipError_t launch_gemv_lds(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 int gemv_lds_rows_per_workgroup();
 int gemv_lds_threads();
+int attn_rows_per_workgroup(int d);
 
 }  // namespace tmm
