@@ -22,7 +22,6 @@ one GPU.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -36,6 +35,7 @@ sys.path.insert(0, ROOT)
 import tiled_matmul_amd as tm  # noqa: E402
 from tiled_matmul_amd import roofline as rl  # noqa: E402
 from tiled_matmul_amd import synth  # noqa: E402
+from tiled_matmul_amd.proftools import kernel_source_sha  # noqa: E402
 
 HBM_TB_S = rl.MI355X_BF16.hbm_tb_s
 MFMA_TFLOPS = rl.MI355X_BF16.peak_tflops
@@ -44,16 +44,6 @@ MALL_BYTES = 256 * 2 ** 20
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
-
-
-def kernel_source_sha() -> str:
-    """Hash of every HIP source and header: identifies the kernels a profile was taken on."""
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "tiled_matmul_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
 
 
 def to_dev(bits, torch):
@@ -115,7 +105,7 @@ def traffic_for(kernel, workload):
             return None
         with open(path) as f:
             t = json.load(f)
-        if t.get("kernel_source_sha") != kernel_source_sha():
+        if t.get("kernel_source_sha") != kernel_source_sha(part):
             return None
         total += t.get("hbm_bytes_per_launch")
     return total
@@ -224,7 +214,7 @@ def mx_leg(args, torch):
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP8_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / FP8_MFMA_TFLOPS,
                      "traffic": traffic_for(kname, name), "flops_per_launch": flops},
-        "kernel_source_sha": kernel_source_sha(),
+        "kernel_source_sha": kernel_source_sha(kname),
     }
 
 
@@ -270,7 +260,7 @@ def attention_leg(args, torch):
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_TFLOPS, "traffic": traffic_for(kname, name),
                      "flops_per_launch": flops},
-        "kernel_source_sha": kernel_source_sha(),
+        "kernel_source_sha": kernel_source_sha(kname),
     }
 
 
@@ -441,8 +431,8 @@ def main():
         copy_leg(args, torch)
         return
     if args.leg == "gemv":
-        print(json.dumps({"gemv": gemv_leg(args, torch, args.gemv_workload),
-                          "kernel_source_sha": kernel_source_sha()}))
+        g = gemv_leg(args, torch, args.gemv_workload)
+        print(json.dumps({"gemv": g, "kernel_source_sha": kernel_source_sha(g["kernel"])}))
         return
 
     if args.workload in synth.ATTN_WORKLOADS:
@@ -466,7 +456,7 @@ def main():
                    "rotating_buffer_sets": len(res["sets"])},
         "pct_mfma_peak": 100.0 * res["tflops"] / MFMA_TFLOPS,
         "roofline": gemm_roofline(res),
-        "kernel_source_sha": kernel_source_sha(),
+        "kernel_source_sha": {k: kernel_source_sha(k) for k in res["kernel"].split("+")},
     }
     if args.leg == "all" and not args.no_gemv:
         result["gemv"] = gemv_leg(args, torch)

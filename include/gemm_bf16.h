@@ -114,8 +114,8 @@ int gemm_bf16_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
  * measurements of each rung).  A variant whose preconditions the arguments do not meet
  * (GEMV with M > 16, or with A, B not 16-byte aligned or lda, ldb, K not multiples of 8;
  * the pipelined, persistent and specialized variants need 4-byte aligned A and B and even
- * lda, ldb and strides; the ping-pong variant 16-byte aligned A and B and lda, ldb, strides
- * and K multiples of 8) returns GEMM_ERR_UNSUPPORTED and does nothing.
+ * lda, ldb and strides; the ping-pong and DTV variants 16-byte aligned A and B and lda, ldb,
+ * strides and K multiples of 8) returns GEMM_ERR_UNSUPPORTED and does nothing.
  * An unknown variant returns GEMM_ERR_ARG.
  */
 int gemm_bf16_variant(int variant, int64_t batch, int64_t M, int64_t N, int64_t K,

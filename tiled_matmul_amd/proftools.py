@@ -5,18 +5,51 @@
         each kernel's first N dispatches (the warm-up launches of a timed run)
     python -m tiled_matmul_amd.proftools traffic --fetch F.csv --write W.csv \
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --kernel SUBSTR \
-        --workload NAME --sha SHA --out profiles/traffic_<kernel>_<workload>.json
+        --workload NAME --plan-kernel ID --out profiles/traffic_<kernel>_<workload>.json
         HBM bytes per launch of the kernel whose name contains SUBSTR, from FETCH_SIZE and
         WRITE_SIZE counter runs (KiB per dispatch), each scaled by the ratio of the known size
-        of a plain copy kernel to what the same counter read for it.
+        of a plain copy kernel to what the same counter read for it; stamped with the source
+        hash of planner kernel ID (ring4_256, gemv_lds, ...).
+    python -m tiled_matmul_amd.proftools sha ID
+        that source hash: the shared headers, the planner and the file that defines kernel ID
 """
 from __future__ import annotations
 
 import argparse
 import csv
+import hashlib
 import json
+import os
 import statistics
 from collections import defaultdict
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+# Sources every kernel is built with (types, waits, tile order, epilogues, MFMA steps) and the
+# host side that plans and launches it.
+SHARED_SOURCES = ("common.hpp", "launch.hpp", "mfma_step.hpp", "gemm_bf16.hip")
+# Planner kernel id -> the file that defines it.
+KERNEL_SOURCE = {
+    "zero_fill": "gemm_simple.hip", "simple_64": "gemm_simple.hip", "mfma_128": "gemm_simple.hip",
+    "pipe_256": "gemm_pipe.hip", "pipe_128": "gemm_pipe.hip", "persist_256": "gemm_pipe.hip",
+    "persist_128": "gemm_pipe.hip", "spec_256": "gemm_pipe.hip", "pingpong_256": "gemm_pingpong.hip",
+    "ring8_256": "gemm_ring.hip", "ring4_256": "gemm_ring.hip", "splitk_reduce": "gemm_ring.hip",
+    "dtv_256": "gemm_dtv.hip", "gemv": "gemv.hip", "gemv_lds": "gemv.hip",
+    "mx_ring_256": "gemm_mx.hip", "mx_simple_64": "gemm_mx.hip",
+    "attn_simple": "attention.hip", "attn_mfma": "attention.hip",
+}
+
+
+def kernel_source_sha(kernel: str | None = None) -> str:
+    """Hash of the sources kernel `kernel` (a planner id) is built from: identifies the code a
+    profile was taken on.  Without a kernel (or for an unknown id): every source."""
+    files = sorted(os.listdir(CSRC))
+    if kernel in KERNEL_SOURCE:
+        files = [*SHARED_SOURCES, KERNEL_SOURCE[kernel]]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
 
 
 def _rows(path):
@@ -54,11 +87,16 @@ def main():
     s.add_argument("--skip-first", type=int, default=0)
     t = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--workload",
-              "--sha", "--out"):
+              "--plan-kernel", "--out"):
         t.add_argument(a, required=True)
+    h = sub.add_parser("sha")
+    h.add_argument("kernel")
     t.add_argument("--copy-kernel", default="copy")
     t.add_argument("--copy-bytes", type=int, required=True)
     a = ap.parse_args()
+    if a.cmd == "sha":
+        print(kernel_source_sha(a.kernel))
+        return
     if a.cmd == "stats":
         for name, v in sorted(kernel_durations(a.trace).items(), key=lambda x: -sum(x[1])):
             v = v[a.skip_first:] if len(v) > a.skip_first else v
@@ -72,7 +110,8 @@ def main():
     f_scale = a.copy_bytes / (cfetch * 1024.0)
     w_scale = a.copy_bytes / (cwrite * 1024.0)
     out = {
-        "kernel": a.kernel, "workload": a.workload, "kernel_source_sha": a.sha,
+        "kernel": a.kernel, "plan_kernel": a.plan_kernel, "workload": a.workload,
+        "kernel_source_sha": kernel_source_sha(a.plan_kernel),
         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
         "dispatches": [nf, nw],
         "copy_calibration": {"bytes": a.copy_bytes, "fetch_kib": cfetch, "write_kib": cwrite,
