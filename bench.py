@@ -7,7 +7,12 @@ is the square 4096^3 GEMM (bf16 inputs N(0,1), fp32 output); the decode GEMV
 
 Timing: W untimed warm-up steps, then K steps between two torch.cuda.synchronize() calls,
 timed with HIP events recorded on the stream the kernels are launched on (the library
-launches on torch's current stream).  Inputs rotate over several buffer sets whose total
+launches on torch's current stream).  The default W = 300 covers the engine clock's settling
+after idle: back-to-back 4096^3 GEMMs take ~144-149 us each over the first 100 launches,
+~108-110 us over the next 100 and ~104 us from then on, so a short warm-up times part of that
+transient.  The default K = 5000 (about 0.5 s at 4096^3) is long enough for the driver's clock
+reading, sampled during the timed steps, to be reported (`sclk_mhz`, and the rate against the
+peak scaled to that clock, `roofline.frac_at_sclk`).  Inputs rotate over several buffer sets whose total
 exceeds the 256 MB Infinity Cache, so no step finds its operands in a cache left warm by
 the previous one.  The GEMV leg captures its launches in a HIP graph (one kernel is a few
 microseconds, below the Python launch overhead) and times graph replays.
@@ -80,19 +85,80 @@ def make_sets(name, torch, min_bytes, la=0, lb=0):
     return (A, B), sets
 
 
-def time_steps(launch, nsets, steps, warmup, torch):
+class SclkSampler:
+    """The engine clock the driver reports (the level marked current in pp_dpm_sclk), read
+    from sysfs every 2 ms by a host thread while the timed steps run; no GPU call."""
+
+    def __init__(self):
+        import glob
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.mhz = []
+
+    def _run(self):
+        import re
+        while not self._stop.is_set():
+            try:
+                with open(self.path) as f:
+                    m = re.search(r"(\d+)\s*[Mm]hz\s*\*", f.read())
+                if m:
+                    self.mhz.append(int(m.group(1)))
+            except OSError:
+                return
+            self._stop.wait(0.002)
+
+    def __enter__(self):
+        import threading
+        if self.path:
+            self._stop = threading.Event()
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.path:
+            self._stop.set()
+            self._t.join()
+
+    # The driver's reading trails the clock (a short run reads partly the idle or warm-up clock
+    # before it), so it is reported only for timed regions at least this long.
+    MIN_WALL_S = 0.5
+
+    def summary(self, wall_s=None):
+        """Median and mean MHz over the samples, or None where sysfs does not expose it or the
+        timed region was shorter than MIN_WALL_S."""
+        if not self.mhz or (wall_s is not None and wall_s < self.MIN_WALL_S):
+            return None
+        v = sorted(self.mhz)
+        return {"median": v[len(v) // 2], "mean": round(sum(v) / len(v), 1), "min": v[0], "max": v[-1],
+                "samples": len(v), "source": "pp_dpm_sclk (driver's current level), sampled every 2 ms"}
+
+
+def time_steps(launch, nsets, steps, warmup, torch, sampler=None, chunk=0):
+    """Average ms per step over `steps` timed steps after `warmup` untimed ones, the wall time,
+    the sampled engine clock and, with chunk > 0, the us per step of each run of `chunk`
+    consecutive steps (events between them; the launches stay back to back)."""
     for i in range(warmup):
         launch(i % nsets)
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps // chunk + 1)] if chunk > 0 else []
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(steps):
-        launch(i % nsets)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return start.elapsed_time(end) / steps, wall
+    sampler = sampler or SclkSampler()
+    with sampler:
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            if chunk > 0 and i % chunk == 0:
+                marks[i // chunk].record()
+            launch(i % nsets)
+        if chunk > 0 and steps % chunk == 0:
+            marks[-1].record()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    per_chunk = [round(marks[j].elapsed_time(marks[j + 1]) * 1e3 / chunk, 2) for j in range(len(marks) - 1)
+                 if chunk > 0 and (j + 1) * chunk <= steps]
+    return start.elapsed_time(end) / steps, wall, sampler.summary(wall), per_chunk
 
 
 def traffic_for(kernel, workload):
@@ -153,7 +219,8 @@ def gemm_leg(args, torch):
 
     log(f"[bench] timing {name}: kernel {kname}, {len(sets)} rotating buffer sets, "
         f"{args.warmup} warm-up + {args.steps} timed steps")
-    ms, wall = time_steps(launch, len(sets), args.steps, args.warmup, torch)
+    ms, wall, sclk, per_chunk = time_steps(launch, len(sets), args.steps, args.warmup, torch,
+                                           chunk=args.chunk)
     flops = rl.flops(M, N, K, batch)
     tflops = flops / (ms * 1e-3) / 1e12
     obytes = 4 if out == tm.GEMM_OUT_FP32 else 2
@@ -163,7 +230,7 @@ def gemm_leg(args, torch):
         "layouts": f"A {args.a_layout}-major, B {args.b_layout}-major",
         "out": "fp32" if out == 0 else "bf16",
         "kernel": kname, "grid": grid, "block": block, "ms": ms, "wall_s": wall,
-        "splits": splits,
+        "splits": splits, "sclk": sclk, "per_chunk": per_chunk,
         "tflops": tflops, "flops": flops, "bytes": nbytes, "A": A, "B": B, "sets": sets,
     }
 
@@ -198,7 +265,7 @@ def mx_leg(args, torch):
 
     log(f"[bench] timing {name}: kernel {kname}, {nsets} rotating buffer sets, "
         f"{args.warmup} warm-up + {args.steps} timed steps")
-    ms, wall = time_steps(launch, nsets, args.steps, args.warmup, torch)
+    ms, wall, sclk, _ = time_steps(launch, nsets, args.steps, args.warmup, torch)
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     fmt = {0: "e4m3", 1: "e5m2"}
@@ -215,6 +282,7 @@ def mx_leg(args, torch):
                      "unit": "TFLOP/s", "frac": tflops / FP8_MFMA_TFLOPS,
                      "traffic": traffic_for(kname, name), "flops_per_launch": flops},
         "kernel_source_sha": kernel_source_sha(kname),
+        "sclk_mhz": sclk,
     }
 
 
@@ -244,7 +312,7 @@ def attention_leg(args, torch):
         tm.attention_fwd(B, Hq, Hkv, Lq, Lk, d, q, k, v, o, None, w["scale"], causal, out)
 
     log(f"[bench] timing {name}: kernel {kname}, {nsets} rotating buffer sets")
-    ms, wall = time_steps(launch, nsets, args.steps, args.warmup, torch)
+    ms, wall, sclk, _ = time_steps(launch, nsets, args.steps, args.warmup, torch)
     # FLOPs of the two products over the (query, key) pairs the mask allows
     pairs = sum(min(Lk, max(0, i + (Lk - Lq) + 1)) for i in range(Lq)) if causal else Lq * Lk
     flops = 4.0 * B * Hq * pairs * d
@@ -261,6 +329,7 @@ def attention_leg(args, torch):
                      "frac": tflops / MFMA_TFLOPS, "traffic": traffic_for(kname, name),
                      "flops_per_launch": flops},
         "kernel_source_sha": kernel_source_sha(kname),
+        "sclk_mhz": sclk,
     }
 
 
@@ -276,6 +345,9 @@ def gemm_roofline(res):
     else:
         r = {"bound": "mfma", "achieved": res["tflops"], "peak": MFMA_TFLOPS, "unit": "TFLOP/s",
              "frac": res["tflops"] / MFMA_TFLOPS}
+    if bound == "mfma" and res.get("sclk"):
+        # the same rate against the dense peak scaled to the clock the driver reported
+        r["frac_at_sclk"] = res["tflops"] / (MFMA_TFLOPS * res["sclk"]["median"] / 2400.0)
     r.update({"traffic": traffic_for(res["kernel"], res["name"]),
               "flops_per_launch": res["flops"], "algorithmic_bytes_per_launch": res["bytes"],
               "intensity_flop_per_byte": ai})
@@ -388,8 +460,10 @@ def copy_leg(args, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=5000)
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="also report the us per step of every run of this many timed steps")
     ap.add_argument("--workload", default="square_4096",
                     choices=sorted(synth.WORKLOADS) + sorted(synth.MX_WORKLOADS)
                     + sorted(synth.ATTN_WORKLOADS))
@@ -456,6 +530,8 @@ def main():
                    "rotating_buffer_sets": len(res["sets"])},
         "pct_mfma_peak": 100.0 * res["tflops"] / MFMA_TFLOPS,
         "roofline": gemm_roofline(res),
+        "sclk_mhz": res["sclk"],
+        **({"us_per_step_by_chunk": {"chunk": args.chunk, "us": res["per_chunk"]}} if args.chunk > 0 else {}),
         "kernel_source_sha": {k: kernel_source_sha(k) for k in res["kernel"].split("+")},
     }
     if args.leg == "all" and not args.no_gemv:

@@ -12,6 +12,15 @@
         hash of planner kernel ID (ring4_256, gemv_lds, ...).
     python -m tiled_matmul_amd.proftools sha ID
         that source hash: the shared headers, the planner and the file that defines kernel ID
+    python -m tiled_matmul_amd.proftools mfma <run_counter_collection.csv> <run_kernel_trace.csv> \
+        --kernel SUBSTR [--peak-tflops P]
+        per dispatch of the kernel whose name contains SUBSTR, from one rocprofv3 run with
+        --kernel-trace and --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+        SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_INSTS_VALU_MFMA_MOPS_F6F4 SQ_LDS_IDX_ACTIVE
+        SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE: the average engine clock (busy cycles of one XCD
+        over the traced duration), the MFMA utilisation (MFMA-busy cycles over the busy cycles
+        of all 1024 SIMDs), the MFMA flops the counters saw (512 per counted op), the rate
+        against the peak at 2.4 GHz and at the measured clock, and LDS activity
 """
 from __future__ import annotations
 
@@ -79,6 +88,46 @@ def counter_per_dispatch(path, counter, substr):
     return statistics.mean(per.values()), len(per)
 
 
+XCDS, CUS, SIMDS, PEAK_GHZ = 8, 256, 1024, 2.4
+
+
+def mfma_summary(counters, trace, substr, peak_tflops=2500.0):
+    """Averages over the dispatches of the kernel whose name contains substr of the counters
+    of one --kernel-trace --pmc run (one row per dispatch and counter, summed over the XCDs)
+    and the derived rates (see the module docstring)."""
+    dur = {}
+    for r in _rows(trace):
+        if substr in r["Kernel_Name"]:
+            dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    per = defaultdict(dict)
+    for r in _rows(counters):
+        if substr in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
+    ids = sorted(set(per) & set(dur), key=int)
+    if not ids:
+        raise SystemExit(f"no dispatch of a kernel containing {substr!r}")
+    out = defaultdict(list)
+    for i in ids:
+        c, ns = per[i], dur[i]
+        cyc = c["GRBM_GUI_ACTIVE"] / XCDS                  # busy cycles of one XCD
+        flops = 512.0 * sum(c.get(k, 0.0) for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                                      "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                                                      "SQ_INSTS_VALU_MFMA_MOPS_F6F4"))
+        ghz = cyc / ns
+        out["us"].append(ns / 1e3)
+        out["ghz"].append(ghz)
+        out["mfma_util"].append(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS))
+        out["lds_util"].append(c.get("SQ_LDS_IDX_ACTIVE", 0.0) / (cyc * CUS))
+        out["lds_bank_conflict"].append(c.get("SQ_LDS_BANK_CONFLICT", 0.0))
+        out["flops"].append(flops)
+        out["tflops"].append(flops / ns / 1e3)
+        out["frac_peak"].append(flops / ns / 1e3 / peak_tflops)
+        out["frac_peak_at_clock"].append(flops / ns / 1e3 / (peak_tflops * ghz / PEAK_GHZ))
+    res = {k: statistics.mean(v) for k, v in out.items()}
+    res["dispatches"] = len(ids)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -91,11 +140,19 @@ def main():
         t.add_argument(a, required=True)
     h = sub.add_parser("sha")
     h.add_argument("kernel")
+    m = sub.add_parser("mfma")
+    m.add_argument("counters")
+    m.add_argument("trace")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--peak-tflops", type=float, default=2500.0)
     t.add_argument("--copy-kernel", default="copy")
     t.add_argument("--copy-bytes", type=int, required=True)
     a = ap.parse_args()
     if a.cmd == "sha":
         print(kernel_source_sha(a.kernel))
+        return
+    if a.cmd == "mfma":
+        print(json.dumps(mfma_summary(a.counters, a.trace, a.kernel, a.peak_tflops)))
         return
     if a.cmd == "stats":
         for name, v in sorted(kernel_durations(a.trace).items(), key=lambda x: -sum(x[1])):
