@@ -35,6 +35,8 @@ extern "C" {
                                   d % 8 == 0)                                                */
 #define ATTN_VARIANT_MFMA 2    /* MFMA tiles of queries x keys, online softmax in registers
                                   (d = 64 or 128; scale > 0; Q, K, V, O 16-byte aligned)     */
+#define ATTN_VARIANT_PIPE 3    /* the same tiles, the next key block's score MFMAs issued
+                                  during this block's softmax (same preconditions)           */
 
 /*
  * The attention forward above.

@@ -285,3 +285,20 @@ def test_mx_validation_and_plan():
     v = tm.gemm_mx_validate
     assert v(0, 0, 64, 64, 64, P, 64, P, 2, P, 64, P, 2, P, 64, 0) == tm.GEMM_OK
     assert v(0, 0, 64, 64, 64, P, 64, P, 1, P, 64, P, 2, P, 64, 0) == tm.GEMM_ERR_ARG
+
+
+def test_attention_plan_variants():
+    """Host-only planning of the attention forward: each variant's kernel, the MFMA kernels'
+    preconditions (d = 64 or 128) and the workgroup grid (128 queries per workgroup)."""
+    P = 1 << 12
+    def aplan(variant, d=128, Lq=4096):
+        return tm.attention_fwd_plan(variant, 1, 32, 8, Lq, 4096, d, P, P, P, P, 0.088, 1, 1, 256)
+    assert aplan(tm.ATTN_VARIANT_MFMA)[:2] == (0, "attn_mfma")
+    assert aplan(tm.ATTN_VARIANT_PIPE)[:2] == (0, "attn_pipe")
+    assert aplan(tm.ATTN_VARIANT_SIMPLE)[:2] == (0, "attn_simple")
+    assert aplan(tm.ATTN_VARIANT_AUTO)[1] in ("attn_mfma", "attn_pipe")
+    assert aplan(tm.ATTN_VARIANT_PIPE)[2] == 32 * 32          # 32 query blocks x 32 heads
+    assert aplan(tm.ATTN_VARIANT_PIPE, d=64)[:2] == (0, "attn_pipe")
+    assert aplan(tm.ATTN_VARIANT_PIPE, d=32)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert aplan(tm.ATTN_VARIANT_AUTO, d=32)[:2] == (0, "attn_simple")
+    assert aplan(4)[0] == tm.GEMM_ERR_ARG

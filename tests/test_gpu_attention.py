@@ -18,7 +18,7 @@ from helpers import OUT_BF16, OUT_FP32, to_device
 
 pytestmark = pytest.mark.gpu
 
-AUTO, SIMPLE, MFMA = tm.ATTN_VARIANT_AUTO, tm.ATTN_VARIANT_SIMPLE, tm.ATTN_VARIANT_MFMA
+AUTO, SIMPLE, MFMA, PIPE = tm.ATTN_VARIANT_AUTO, tm.ATTN_VARIANT_SIMPLE, tm.ATTN_VARIANT_MFMA, tm.ATTN_VARIANT_PIPE
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -77,7 +77,7 @@ def test_attention_parity(B, Hq, Hkv, Lq, Lk, d, causal):
     scale = 1.0 / math.sqrt(d)
     P = 1 << 12
     kname = tm.attention_fwd_plan(AUTO, B, Hq, Hkv, Lq, Lk, d, P, P, P, P, scale, causal, 0)[1]
-    variants = [AUTO, SIMPLE] + ([MFMA] if kname == "attn_mfma" else [])
+    variants = [AUTO, SIMPLE] + ([MFMA, PIPE] if kname in ("attn_mfma", "attn_pipe") else [])
     for variant in variants:
         for out_dtype in (OUT_FP32, OUT_BF16):
             o, lse = run(Q, K, V, scale, causal, out_dtype, variant)
@@ -101,10 +101,11 @@ def test_attention_empty_and_errors():
             tm.attention_fwd(*args, to_device(Q), to_device(K), to_device(V), O, LSE, 0.1, 1,
                              OUT_FP32)
         assert e.value.status == code
-    with pytest.raises(tm.GemmError) as e:
-        tm.attention_fwd_variant(MFMA, 1, 2, 1, 8, 8, 32, to_device(Q), to_device(K),
-                                 to_device(V), O, LSE, 0.1, 1, OUT_FP32)
-    assert e.value.status == tm.GEMM_ERR_UNSUPPORTED
+    for variant in (MFMA, PIPE):   # the MFMA kernels take d = 64 and 128 only
+        with pytest.raises(tm.GemmError) as e:
+            tm.attention_fwd_variant(variant, 1, 2, 1, 8, 8, 32, to_device(Q), to_device(K),
+                                     to_device(V), O, LSE, 0.1, 1, OUT_FP32)
+        assert e.value.status == tm.GEMM_ERR_UNSUPPORTED
 
 
 def test_attention_lse_optional_and_deterministic():
@@ -113,17 +114,19 @@ def test_attention_lse_optional_and_deterministic():
     Qd, Kd, Vd = to_device(Q), to_device(K), to_device(V)
     O1 = torch.empty((1, 4, 96, 128), device="cuda")
     O2 = torch.empty((1, 4, 96, 128), device="cuda")
-    tm.attention_fwd(1, 4, 2, 96, 96, 128, Qd, Kd, Vd, O1, None, 0.09, 1, OUT_FP32)
-    tm.attention_fwd(1, 4, 2, 96, 96, 128, Qd, Kd, Vd, O2, None, 0.09, 1, OUT_FP32)
-    torch.cuda.synchronize()
-    assert torch.equal(O1, O2)
+    for variant in (AUTO, MFMA, PIPE):
+        tm.attention_fwd_variant(variant, 1, 4, 2, 96, 96, 128, Qd, Kd, Vd, O1, None, 0.09, 1, OUT_FP32)
+        tm.attention_fwd_variant(variant, 1, 4, 2, 96, 96, 128, Qd, Kd, Vd, O2, None, 0.09, 1, OUT_FP32)
+        torch.cuda.synchronize()
+        assert torch.equal(O1, O2), variant
 
 
+@pytest.mark.parametrize("variant", [AUTO, MFMA, PIPE])
 @pytest.mark.parametrize("name", sorted(synth.ATTN_WORKLOADS))
-def test_attention_workloads_full_size_sampled(name):
+def test_attention_workloads_full_size_sampled(name, variant):
     w = synth.ATTN_WORKLOADS[name]
     Q, K, V = synth.make_attention_inputs(name)
-    o, lse = run(Q, K, V, w["scale"], w["causal"], w["out"])
+    o, lse = run(Q, K, V, w["scale"], w["causal"], w["out"], variant)
     B, Hq = w["B"], w["Hq"]
     rng = np.random.default_rng(3)
     heads = sorted({(0, 0), (B - 1, Hq - 1)} | {(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(3)})

@@ -48,6 +48,7 @@ GEMM_MX_VARIANT_RING = 2
 ATTN_VARIANT_AUTO = 0
 ATTN_VARIANT_SIMPLE = 1
 ATTN_VARIANT_MFMA = 2
+ATTN_VARIANT_PIPE = 3
 
 GEMM_VARIANT_AUTO = 0
 GEMM_VARIANT_SIMPLE = 1

@@ -138,6 +138,11 @@ constexpr int BKV = 64;
 #define TMM_ATTN_SETPRIO 1
 #endif
 
+// Vector instructions the pipelined attention kernel places after each score MFMA.
+#ifndef TMM_ATTN_PIPE_VALU
+#define TMM_ATTN_PIPE_VALU 6
+#endif
+
 int attn_rows_per_workgroup(int d) { return 64 * (d == 128 ? TMM_ATTN_QT128 : TMM_ATTN_QT64); }
 
 // Max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that hold one query's
@@ -155,6 +160,35 @@ __device__ __forceinline__ float group4_sum(float v) {
     v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Work item (batch b, query head h, query block qb) of the MFMA attention workgroup with grid
+// (query blocks, Hq, B).  Workgroups are dispatched in linear order (x fastest) and handed to
+// the 8 XCDs round-robin; the linear id is mapped so that each XCD gets a contiguous range of
+// the order (b, K/V head, query block, query head of the group): the query blocks of one K/V
+// head then run on one XCD, whose L2 serves their repeated reads of that head's K and V, and
+// within an XCD the query blocks are started in launch-priority order (causal: the blocks
+// with the most keys first) across the heads of the group.
+#ifndef TMM_ATTN_XCD_MAP
+#define TMM_ATTN_XCD_MAP 1   // 0: the plain order (b = z, h = y, query block from x)
+#endif
+__device__ __forceinline__ void attn_block_of(const AttnArgs& g, int64_t& b, int64_t& h, int64_t& qb) {
+    if (!TMM_ATTN_XCD_MAP) {
+        b = blockIdx.z, h = blockIdx.y;
+        qb = g.causal ? static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x : blockIdx.x;
+        return;
+    }
+    constexpr int64_t XCD = 8;
+    const int64_t nqb = gridDim.x, total = nqb * gridDim.y * gridDim.z;
+    const int64_t t = blockIdx.x + nqb * (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z);
+    const int64_t per = total / XCD, extra = total % XCD, x = t % XCD, local = t / XCD;
+    const int64_t L = x < extra ? x * (per + 1) + local : extra * (per + 1) + (x - extra) * per + local;
+    const int64_t G = g.Hq / g.Hkv;
+    const int64_t gi = L % G, rest = L / G, qi = rest % nqb, rest2 = rest / nqb;
+    const int64_t kvh = rest2 % g.Hkv;
+    b = rest2 / g.Hkv;
+    h = kvh * G + gi;
+    qb = g.causal ? nqb - 1 - qi : qi;
 }
 
 template <int D, int OUT, int QT>
@@ -181,10 +215,9 @@ __global__ __launch_bounds__(256, QT == 2 ? 2 : 1) void attn_mfma_kernel(AttnArg
 
     const int lane = lane_id(), w = wave_id();
     const int lg = lane >> 4, lq = lane & 15;
-    const int64_t h = blockIdx.y, b = blockIdx.z;
+    int64_t b, h, qb;
+    attn_block_of(g, b, h, qb);
     const int64_t gk = h / (g.Hq / g.Hkv);
-    // Causal rows near the end see the most keys: start those workgroups first.
-    const int64_t qb = g.causal ? static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x : blockIdx.x;
     const int64_t q0 = qb * BQ, qw = q0 + WQ * w;
     const int64_t shift = g.Lk - g.Lq;                 // causal: key j <= query i + shift
     const float sl2 = g.scale * 1.4426950408889634f;    // scores in base 2
@@ -400,9 +433,267 @@ __global__ __launch_bounds__(256, QT == 2 ? 2 : 1) void attn_mfma_kernel(AttnArg
     }
 }
 
+// attn_pipe_kernel (d = 64 or 128): the tiles, LDS layouts and arithmetic of attn_mfma_kernel
+// (32 queries per wave, 64-key blocks, S^T = K Q^T, base-2 online softmax with selective
+// rescaling, O^T += V^T P^T from transposing reads), with the score products of block j + 1
+// issued while block j's softmax runs.  In one wave the MFMAs of a block wait for its
+// softmax and the softmax for its MFMAs; here the score MFMAs of the next block do not
+// depend on the softmax of this one, so the two are interleaved (one MFMA, then a group of
+// VALU instructions, fixed with scheduling groups) and the matrix and vector units run at
+// the same time.  K is loaded two blocks ahead (its fragments are read one block early), V
+// one block ahead; both rings have two slots, as before.
+//   iteration j (scores of block j already in registers, masked):
+//     load K(j+2) into K(j)'s slot, V(j+1) into V(j-1)'s slot; wait for K(j+1), V(j); barrier
+//     scores of block j+1 (K(j+1) fragments, MFMAs)   interleaved with   softmax of block j
+//     rescale O where the reference maximum moved; mask block j+1's scores if it is an edge
+//     O^T += V(j)^T P(j)^T; barrier
+// The scores of the block past the last (read from zeros) are computed and dropped.
+template <int D, int OUT>
+__global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs g) {
+    using namespace at;
+    constexpr int QT = 2, WQ = 32, BQ = 128;
+    constexpr int ROWB = D * 2, CPR = D / 8, TILE = BKV * ROWB, RPI = 1024 / ROWB;
+    constexpr int LPT = TILE / 1024 / 4;   // load instructions per wave per tile
+    constexpr int KS = D / 32, DT = D / 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t kl[2][TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t vl[2][TILE];
+    constexpr int RP = 256 / ROWB;
+    auto kswz = [](int r) { return r & (CPR - 1); };
+    auto vswz = [](int r) { return 2 * ((r / RP) & (CPR / 2 - 1)); };
+
+    const int lane = lane_id(), w = wave_id();
+    const int lg = lane >> 4, lq = lane & 15;
+    int64_t b, h, qb;
+    attn_block_of(g, b, h, qb);
+    const int64_t gk = h / (g.Hq / g.Hkv);
+    const int64_t q0 = qb * BQ, qw = q0 + WQ * w;
+    const int64_t shift = g.Lk - g.Lq;
+    const float sl2 = g.scale * 1.4426950408889634f;
+    const uint16_t* Kb = g.K + (b * g.Hkv + gk) * g.Lk * D;
+    const uint16_t* Vb = g.V + (b * g.Hkv + gk) * g.Lk * D;
+    const int64_t q_last = min<int64_t>(q0 + BQ, g.Lq) - 1;
+    int64_t kend = g.Lk;
+    if (g.causal) kend = max<int64_t>(0, min<int64_t>(g.Lk, q_last + shift + 1));
+    const int nblk = static_cast<int>((kend + BKV - 1) / BKV);
+
+    bf16x8 qf[QT][KS];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int64_t qi = qw + 16 * qt + lq;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (qi < g.Lq) v = *reinterpret_cast<const u32x4*>(g.Q + ((b * g.Hq + h) * g.Lq + qi) * D + 32 * kk + 8 * lg);
+            qf[qt][kk] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    // Direct-to-LDS loads of the K or V tile of key block j (rows past Lk, or a block wholly
+    // past it, read zeros).
+    const int lrow = lane / CPR, lchunk = lane % CPR;
+    auto load_tile = [&](const uint16_t* base, bool is_v, int j, uint8_t* dst) {
+        const int64_t kv0 = static_cast<int64_t>(j) * BKV;
+        const int64_t rows = max<int64_t>(0, min<int64_t>(BKV, g.Lk - kv0));
+        const auto r = make_rsrc(rows > 0 ? base + kv0 * D : base, static_cast<uint32_t>(rows * ROWB));
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int row = (4 * i + w) * RPI + lrow;
+            const uint32_t off = static_cast<uint32_t>(row * ROWB) +
+                                 16u * static_cast<uint32_t>(lchunk ^ (is_v ? vswz(row) : kswz(row)));
+            load_lds_16(r, dst + (4 * i + w) * 1024, off, 0u);
+        }
+    };
+    // S^T of the key block whose K tile is at Kt (4 key tiles x 2 query tiles).
+    auto scores = [&](f32x4 (&sc)[4][QT], const uint8_t* Kt) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) sc[t][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            bf16x8 kf[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = 16 * t + lq;
+                kf[t] = *reinterpret_cast<const bf16x8*>(Kt + r * ROWB + 16 * ((4 * kk + lg) ^ kswz(r)));
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) sc[t][qt] = mfma_16x16x32(kf[t], qf[qt][kk], sc[t][qt]);
+        }
+    };
+    // Masked scores of block j at -inf (only blocks that reach past Lk or the diagonal): key
+    // kv0 + o of query row qi is allowed when o < lim(qi), lim = min(Lk, qi + shift + 1) - kv0
+    // clamped to [0, BKV]; one compare and select per score, no branches.
+    auto mask = [&](f32x4 (&sc)[4][QT], int j) {
+        const int64_t kv0 = static_cast<int64_t>(j) * BKV;
+        if (kv0 + BKV > g.Lk || (g.causal && kv0 + BKV - 1 > qw + shift)) {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                int64_t e = g.Lk;
+                if (g.causal) e = min<int64_t>(e, qw + 16 * qt + lq + shift + 1);
+                const int lim = static_cast<int>(max<int64_t>(0, min<int64_t>(BKV, e - kv0)));
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sc[t][qt][r] = 16 * t + 4 * lg + r < lim ? sc[t][qt][r] : -INFINITY;
+            }
+        }
+    };
+
+    f32x4 oacc[DT][QT];
+    float m[QT], l[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+        for (int i = 0; i < DT; ++i) oacc[i][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[qt] = -INFINITY, l[qt] = 0.f;
+    }
+
+    f32x4 sc[4][QT];   // scores of the block being finished
+    if (nblk > 0) {
+        load_tile(Kb, false, 0, kl[0]);
+        load_tile(Vb, true, 0, vl[0]);
+        load_tile(Kb, false, 1, kl[1]);
+        wait_vmcnt<2 * LPT>();   // K(0) has landed (this wave) ...
+        barrier();               // ... and every wave's
+        scores(sc, kl[0]);
+        mask(sc, 0);
+        barrier();               // every wave has read K(0) before K(2) is loaded into its slot
+    }
+    for (int j = 0; j < nblk; ++j) {
+        load_tile(Kb, false, j + 2, kl[j & 1]);
+        load_tile(Vb, true, j + 1, vl[(j + 1) & 1]);
+        wait_vmcnt<2 * LPT>();   // K(j+1) and V(j) have landed (this wave) ...
+        barrier();               // ... and every wave's
+
+        // Scores of block j+1 interleaved with the softmax of block j.
+        f32x4 sn[4][QT];
+        scores(sn, kl[(j + 1) & 1]);
+        u32x2 pb[QT][4];
+        float alpha[QT];
+        bool need[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            float mx4[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                mx4[t] = fmaxf(fmaxf(sc[t][qt][0], sc[t][qt][1]), fmaxf(sc[t][qt][2], sc[t][qt][3]));
+            float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+            mx = group4_max(mx) * sl2;
+            need[qt] = m[qt] == -INFINITY || mx > m[qt] + 8.f;
+            const float mn = need[qt] ? mx : m[qt];
+            alpha[qt] = !need[qt] ? 1.f : (m[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[qt] - mn));
+            const float nref = mn == -INFINITY ? 0.f : -mn;
+            float sum4[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float p[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sc[t][qt][r], sl2, nref));
+                sum4[t] = (p[0] + p[1]) + (p[2] + p[3]);
+                pb[qt][t] = u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+            }
+            l[qt] = l[qt] * alpha[qt] + group4_sum((sum4[0] + sum4[1]) + (sum4[2] + sum4[3]));
+            m[qt] = mn;
+        }
+        // Scheduling groups: for every score MFMA, one MFMA and then up to TMM_ATTN_PIPE_VALU
+        // vector instructions of the softmax (the fragment reads are left to the scheduler).
+#pragma unroll
+        for (int i = 0; i < 4 * KS * QT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, TMM_ATTN_PIPE_VALU, 0);   // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+            if (__builtin_amdgcn_ballot_w64(need[qt]) != 0) {   // wave-uniform
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) oacc[dt][qt][r] *= alpha[qt];
+            }
+        mask(sn, j + 1);
+
+        // O^T += V(j)^T P(j)^T, as in attn_mfma_kernel.
+        const uint8_t* Vt = vl[j & 1];
+        u32x2 hv[2][DT][2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                    const int r = 16 * (2 * st + e2) + lane / 4;
+                    const int c = 2 * dt + ((lane & 3) >> 1);
+                    const int off = r * ROWB + 16 * (c ^ vswz(r)) + 8 * (lane & 1);
+                    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(Vt + off)));
+                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hv[st][dt][e2]) : "v"(addr) : "memory");
+                }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            bf16x8 pf[QT];
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+                pf[qt] = __builtin_bit_cast(bf16x8, u32x4{pb[qt][2 * st][0], pb[qt][2 * st][1], pb[qt][2 * st + 1][0],
+                                                          pb[qt][2 * st + 1][1]});
+            __builtin_amdgcn_sched_barrier(0);
+            if (st == 0)
+                wait_cnt<63, 2 * DT - 1>();
+            else
+                wait_cnt<63, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[st][dt][0], hv[st][dt][1], 0, 1, 2, 3));
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma_16x16x32(vf, pf[qt], oacc[dt][qt]);
+            }
+        }
+        barrier();   // every wave is done with K(j+1) and V(j) before their slots are refilled
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) sc[t][qt] = sn[t][qt];
+    }
+    wait_vmcnt<0>();   // the loads past the last block have landed before the workgroup ends
+
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int64_t qi = qw + 16 * qt + lq;
+        if (qi >= g.Lq) continue;
+        const float inv = l[qt] > 0.f ? 1.f / l[qt] : 0.f;
+        const int64_t orow = ((b * g.Hq + h) * g.Lq + qi) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 v = {oacc[dt][qt][0] * inv, oacc[dt][qt][1] * inv, oacc[dt][qt][2] * inv, oacc[dt][qt][3] * inv};
+            const int64_t c = 16 * dt + 4 * lg;
+            if constexpr (OUT == OUT_F32)
+                *reinterpret_cast<f32x4*>(static_cast<float*>(g.O) + orow + c) = v;
+            else
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.O) + orow + c) =
+                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+        if (g.LSE && lg == 0)
+            g.LSE[(b * g.Hq + h) * g.Lq + qi] = l[qt] > 0.f ? (m[qt] + log2f(l[qt])) * 0.6931471805599453f : -INFINITY;
+    }
+}
+
 hipError_t launch_attention(const AttnArgs& g, int out, const Plan& p, hipStream_t s) {
     const dim3 grid(p.grid_x, p.grid_y, p.grid_z);
-    if (p.kernel == K_ATTN_MFMA) {
+    if (p.kernel == K_ATTN_PIPE) {
+        if (g.d == 128 && out == OUT_F32)
+            hipLaunchKernelGGL((attn_pipe_kernel<128, OUT_F32>), grid, dim3(256), 0, s, g);
+        else if (g.d == 128)
+            hipLaunchKernelGGL((attn_pipe_kernel<128, OUT_BF16>), grid, dim3(256), 0, s, g);
+        else if (out == OUT_F32)
+            hipLaunchKernelGGL((attn_pipe_kernel<64, OUT_F32>), grid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((attn_pipe_kernel<64, OUT_BF16>), grid, dim3(256), 0, s, g);
+    } else if (p.kernel == K_ATTN_MFMA) {
         constexpr int Q1 = TMM_ATTN_QT128, Q6 = TMM_ATTN_QT64;
         if (g.d == 128 && out == OUT_F32)
             hipLaunchKernelGGL((attn_mfma_kernel<128, OUT_F32, Q1>), grid, dim3(256), 0, s, g);

@@ -550,18 +550,25 @@ bool attn_mfma_ok(const AttnShape& s) {
     return s.Lk * s.d * 2 < k2G && cdiv(s.Lq, 128) < k2G;
 }
 
+// AUTO's choice between the two MFMA attention kernels (1: attn_pipe, 0: attn_mfma).
+#ifndef TMM_ATTN_AUTO_PIPE
+#define TMM_ATTN_AUTO_PIPE 0
+#endif
+
 int plan_attn(int variant, const AttnShape& s, int cus, Plan& p) {
     (void)cus;
-    if (variant < ATTN_VARIANT_AUTO || variant > ATTN_VARIANT_MFMA) return GEMM_ERR_ARG;
+    if (variant < ATTN_VARIANT_AUTO || variant > ATTN_VARIANT_PIPE) return GEMM_ERR_ARG;
     p = Plan{};
     if (s.Lq == 0) {
         p.kernel = K_NONE;
         return GEMM_OK;
     }
     const bool mfma = attn_mfma_ok(s);
-    if (variant == ATTN_VARIANT_MFMA && !mfma) return GEMM_ERR_UNSUPPORTED;
+    if ((variant == ATTN_VARIANT_MFMA || variant == ATTN_VARIANT_PIPE) && !mfma) return GEMM_ERR_UNSUPPORTED;
     if (mfma && variant != ATTN_VARIANT_SIMPLE) {
-        p.kernel = K_ATTN_MFMA;
+        p.kernel = variant == ATTN_VARIANT_PIPE || (variant == ATTN_VARIANT_AUTO && TMM_ATTN_AUTO_PIPE)
+                       ? K_ATTN_PIPE
+                       : K_ATTN_MFMA;
         p.grid_x = static_cast<int>(cdiv(s.Lq, attn_rows_per_workgroup(static_cast<int>(s.d))));
         p.grid_y = static_cast<int>(s.Hq);
         p.grid_z = static_cast<int>(s.B);
@@ -780,6 +787,7 @@ const char* gemm_bf16_kernel_name(int k) {
         case K_MX_SIMPLE_64: return "mx_simple_64";
         case K_ATTN_SIMPLE: return "attn_simple";
         case K_ATTN_MFMA: return "attn_mfma";
+        case K_ATTN_PIPE: return "attn_pipe";
         case K_GEMV: return "gemv";
         case K_GEMV_LDS: return "gemv_lds";
         default: return "?";

@@ -29,7 +29,8 @@ enum KernelId {
     K_ATTN_SIMPLE = 16,     // attention forward: one wave per query row (any d <= 256)
     K_ATTN_MFMA = 17,       //   MFMA tiles of queries x keys, online softmax (d = 64, 128)
     K_DTV_256 = 18,         // steps 4-6 with the A operand loaded straight into MFMA registers, B ring in LDS
-    K_COUNT = 19
+    K_ATTN_PIPE = 19,       //   same, the next block's score MFMAs interleaved with this block's softmax
+    K_COUNT = 20
 };
 
 // Launch shape chosen for a problem (filled by the planner, consumed by the launchers).

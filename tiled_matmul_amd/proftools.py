@@ -44,7 +44,7 @@ KERNEL_SOURCE = {
     "ring8_256": "gemm_ring.hip", "ring4_256": "gemm_ring.hip", "splitk_reduce": "gemm_ring.hip",
     "dtv_256": "gemm_dtv.hip", "gemv": "gemv.hip", "gemv_lds": "gemv.hip",
     "mx_ring_256": "gemm_mx.hip", "mx_simple_64": "gemm_mx.hip",
-    "attn_simple": "attention.hip", "attn_mfma": "attention.hip",
+    "attn_simple": "attention.hip", "attn_mfma": "attention.hip", "attn_pipe": "attention.hip",
 }
 
 
