@@ -143,7 +143,12 @@ constexpr int BKV = 64;
 #define TMM_ATTN_PIPE_VALU 6
 #endif
 
-int attn_rows_per_workgroup(int d) { return 64 * (d == 128 ? TMM_ATTN_QT128 : TMM_ATTN_QT64); }
+// Query rows per workgroup of each MFMA attention kernel (attn_pipe_kernel: 2 query tiles of 16
+// per wave, always).
+int attn_rows_per_workgroup(int kernel, int d) {
+    if (kernel == K_ATTN_PIPE) return 128;
+    return 64 * (d == 128 ? TMM_ATTN_QT128 : TMM_ATTN_QT64);
+}
 
 // Max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups that hold one query's
 // scores) with gfx950's row swaps, in the VALU: permlane16_swap(x, x) leaves rows (0, 0, 2, 2)

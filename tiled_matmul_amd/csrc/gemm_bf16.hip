@@ -569,7 +569,7 @@ int plan_attn(int variant, const AttnShape& s, int cus, Plan& p) {
         p.kernel = variant == ATTN_VARIANT_PIPE || (variant == ATTN_VARIANT_AUTO && TMM_ATTN_AUTO_PIPE)
                        ? K_ATTN_PIPE
                        : K_ATTN_MFMA;
-        p.grid_x = static_cast<int>(cdiv(s.Lq, attn_rows_per_workgroup(static_cast<int>(s.d))));
+        p.grid_x = static_cast<int>(cdiv(s.Lq, attn_rows_per_workgroup(p.kernel, static_cast<int>(s.d))));
         p.grid_y = static_cast<int>(s.Hq);
         p.grid_z = static_cast<int>(s.B);
         p.block = 256;

@@ -56,6 +56,6 @@ hipError_t launch_attention(const AttnArgs& g, int out, const Plan& p, hipStream
 hipError_t launch_gemv_lds(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 int gemv_lds_rows_per_workgroup();
 int gemv_lds_threads();
-int attn_rows_per_workgroup(int d);
+int attn_rows_per_workgroup(int kernel, int d);
 
 }  // namespace tmm
