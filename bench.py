@@ -161,17 +161,20 @@ def time_steps(launch, nsets, steps, warmup, torch, sampler=None, chunk=0):
     return start.elapsed_time(end) / steps, wall, sampler.summary(wall), per_chunk
 
 
-def traffic_for(kernel, workload):
+def traffic_for(kernel, workload, grid=None, block=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel sources; else None.  "a+b" (a call of two kernels) sums both."""
+    the current sources of the kernel and (where the summary records it) the same launch
+    shape of its first kernel; else None.  "a+b" (a call of two kernels) sums both."""
     total = 0
-    for part in kernel.split("+"):
+    for i, part in enumerate(kernel.split("+")):
         path = os.path.join(ROOT, "profiles", f"traffic_{part}_{workload}.json")
         if not os.path.exists(path):
             return None
         with open(path) as f:
             t = json.load(f)
         if t.get("kernel_source_sha") != kernel_source_sha(part):
+            return None
+        if i == 0 and t.get("grid") is not None and (t.get("grid"), t.get("block")) != (grid, block):
             return None
         total += t.get("hbm_bytes_per_launch")
     return total
@@ -280,7 +283,7 @@ def mx_leg(args, torch):
                    "kernel": kname, "grid": grid, "block": block, "rotating_buffer_sets": nsets},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP8_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / FP8_MFMA_TFLOPS,
-                     "traffic": traffic_for(kname, name), "flops_per_launch": flops},
+                     "traffic": traffic_for(kname, name, grid, block), "flops_per_launch": flops},
         "kernel_source_sha": kernel_source_sha(kname),
         "sclk_mhz": sclk,
     }
@@ -326,7 +329,7 @@ def attention_leg(args, torch):
                                f"{'causal' if causal else 'full'}, {'fp32' if out == 0 else 'bf16'} out",
                    "kernel": kname, "grid": grid, "block": block, "rotating_buffer_sets": nsets},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_TFLOPS, "traffic": traffic_for(kname, name),
+                     "frac": tflops / MFMA_TFLOPS, "traffic": traffic_for(kname, name, grid, block),
                      "flops_per_launch": flops},
         "kernel_source_sha": kernel_source_sha(kname),
         "sclk_mhz": sclk,
@@ -348,7 +351,7 @@ def gemm_roofline(res):
     if bound == "mfma" and res.get("sclk"):
         # the same rate against the dense peak scaled to the clock the driver reported
         r["frac_at_sclk"] = res["tflops"] / (MFMA_TFLOPS * res["sclk"]["median"] / 2400.0)
-    r.update({"traffic": traffic_for(res["kernel"], res["name"]),
+    r.update({"traffic": traffic_for(res["kernel"], res["name"], res["grid"], res["block"]),
               "flops_per_launch": res["flops"], "algorithmic_bytes_per_launch": res["bytes"],
               "intensity_flop_per_byte": ai})
     return r
@@ -397,7 +400,7 @@ def gemv_leg(args, torch, name="gemv_m1"):
         "kernel": kname, "grid": grid, "block": block, "rotating_weight_buffers": n,
         "timing": "HIP events around replays of a captured HIP graph of back-to-back launches",
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_TB_S * 1e3, "unit": "GB/s",
-                     "frac": gbs / (HBM_TB_S * 1e3), "traffic": traffic_for(kname, name),
+                     "frac": gbs / (HBM_TB_S * 1e3), "traffic": traffic_for(kname, name, grid, block),
                      "algorithmic_bytes_per_launch": nbytes},
     }
 

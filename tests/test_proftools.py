@@ -29,6 +29,9 @@ def test_hash_covers_exactly_the_kernel_sources(tmp_path, monkeypatch):
         f.write("\n// edit\n")
     assert pt.kernel_source_sha("ring4_256") == ring
     assert pt.kernel_source_sha("attn_mfma") != attn
+    with open(src / "gemm_bf16.hip", "a") as f:          # the host planner is not hashed
+        f.write("\n// edit\n")
+    assert pt.kernel_source_sha("ring4_256") == ring
     with open(src / "common.hpp", "a") as f:             # a shared header changes
         f.write("\n// edit\n")
     assert pt.kernel_source_sha("ring4_256") != ring

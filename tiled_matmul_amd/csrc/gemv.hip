@@ -29,8 +29,9 @@ namespace tmm {
 #define TMM_GEMV_AUX 2
 #endif
 
-template <int OUT, int UNROLL>
+template <int OUT, int UNROLL, bool PAIRS>
 __global__ __launch_bounds__(512) void gemv_kernel(GemmArgs g) {
+    static_assert(!PAIRS || UNROLL % 2 == 0, "pairs of steps");
     constexpr int WAVES = 8, KX = 4096;
     constexpr int XST = KX * 2 + 16;   // LDS pitch of a row of X: 16 bytes of padding move
                                        // each row 4 banks, so a fragment read is conflict-free
@@ -64,10 +65,17 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemmArgs g) {
         asm volatile("" ::: "memory");   // the W loads below stay behind the X loads
         const int steps = static_cast<int>((min(K - k0, static_cast<uint32_t>(KX)) + 31) / 32);
         u32x4 wv[UNROLL];
+        // k step of load u of the group starting at s0 (= w + i WAVES UNROLL): with PAIRS,
+        // steps 2 j and 2 j + 1 (the two halves of each 128-byte line of a W row) go to one
+        // wave back to back; otherwise the waves take steps in turn.
+        auto step_of = [&](int s0, int u) {
+            if constexpr (PAIRS) return (s0 - w) + 2 * (w + WAVES * (u / 2)) + (u % 2);
+            return s0 + u * WAVES;
+        };
         auto load_w = [&](int s0) {
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
-                const int s = s0 + u * WAVES;
+                const int s = step_of(s0, u);
                 const uint32_t k = k0 + static_cast<uint32_t>(s) * 32u + 8u * c;   // this lane's chunk
                 wv[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, s < steps && k < K ? vw : OOB, 2u * (k0 + 32u * s),
                                                               TMM_GEMV_AUX);
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemmArgs g) {
             if (s0 != w) load_w(s0);
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
-                const int s = s0 + u * WAVES;
+                const int s = step_of(s0, u);
                 if (s < steps) {   // wave-uniform
                     const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xfrag + s * 64);
                     acc = mfma_16x16x32(__builtin_bit_cast(bf16x8, wv[u]), xv, acc);
@@ -114,6 +122,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemmArgs g) {
         }
     }
 }
+
+// Each wave loads both 64-byte halves of a W row's 128-byte lines back to back (1) or the
+// waves take the 32-deep k steps in turn (0).
+#ifndef TMM_GEMV_PAIRS
+#define TMM_GEMV_PAIRS 1
+#endif
 
 // W loads in flight per wave (16 covers a whole phase of 4096 k at once).
 #ifndef TMM_GEMV_UNROLL
@@ -273,10 +287,11 @@ int gemv_lds_threads() { return 64 * TMM_LDS_WAVES; }
 
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
     constexpr int U = TMM_GEMV_UNROLL;
+    constexpr bool PR = TMM_GEMV_PAIRS != 0;
     if (out == OUT_F32)
-        hipLaunchKernelGGL((gemv_kernel<OUT_F32, U>), dim3(p.grid_x), dim3(512), 0, s, g);
+        hipLaunchKernelGGL((gemv_kernel<OUT_F32, U, PR>), dim3(p.grid_x), dim3(512), 0, s, g);
     else
-        hipLaunchKernelGGL((gemv_kernel<OUT_BF16, U>), dim3(p.grid_x), dim3(512), 0, s, g);
+        hipLaunchKernelGGL((gemv_kernel<OUT_BF16, U, PR>), dim3(p.grid_x), dim3(512), 0, s, g);
     return hipGetLastError();
 }
 

@@ -9,9 +9,10 @@
         HBM bytes per launch of the kernel whose name contains SUBSTR, from FETCH_SIZE and
         WRITE_SIZE counter runs (KiB per dispatch), each scaled by the ratio of the known size
         of a plain copy kernel to what the same counter read for it; stamped with the source
-        hash of planner kernel ID (ring4_256, gemv_lds, ...).
+        hash of planner kernel ID (ring4_256, gemv_lds, ...) and, with --grid G --block B, the
+        launch shape it was measured on.
     python -m tiled_matmul_amd.proftools sha ID
-        that source hash: the shared headers, the planner and the file that defines kernel ID
+        that source hash: the shared device headers and the file that defines kernel ID
     python -m tiled_matmul_amd.proftools mfma <run_counter_collection.csv> <run_kernel_trace.csv> \
         --kernel SUBSTR [--peak-tflops P]
         per dispatch of the kernel whose name contains SUBSTR, from one rocprofv3 run with
@@ -33,9 +34,10 @@ import statistics
 from collections import defaultdict
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-# Sources every kernel is built with (types, waits, tile order, epilogues, MFMA steps) and the
-# host side that plans and launches it.
-SHARED_SOURCES = ("common.hpp", "launch.hpp", "mfma_step.hpp", "gemm_bf16.hip")
+# Device sources every kernel is built with (types, waits, tile order, epilogues, MFMA steps).
+# The host planner is not hashed: a summary records the launch it was measured on (kernel,
+# grid, block), which bench.py compares with the launch it makes.
+SHARED_SOURCES = ("common.hpp", "launch.hpp", "mfma_step.hpp")
 # Planner kernel id -> the file that defines it.
 KERNEL_SOURCE = {
     "zero_fill": "gemm_simple.hip", "simple_64": "gemm_simple.hip", "mfma_128": "gemm_simple.hip",
@@ -138,6 +140,8 @@ def main():
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--workload",
               "--plan-kernel", "--out"):
         t.add_argument(a, required=True)
+    t.add_argument("--grid", type=int)
+    t.add_argument("--block", type=int)
     h = sub.add_parser("sha")
     h.add_argument("kernel")
     m = sub.add_parser("mfma")
@@ -168,7 +172,7 @@ def main():
     w_scale = a.copy_bytes / (cwrite * 1024.0)
     out = {
         "kernel": a.kernel, "plan_kernel": a.plan_kernel, "workload": a.workload,
-        "kernel_source_sha": kernel_source_sha(a.plan_kernel),
+        "kernel_source_sha": kernel_source_sha(a.plan_kernel), "grid": a.grid, "block": a.block,
         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
         "dispatches": [nf, nw],
         "copy_calibration": {"bytes": a.copy_bytes, "fetch_kib": cfetch, "write_kib": cwrite,
