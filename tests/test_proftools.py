@@ -36,3 +36,9 @@ def test_hash_covers_exactly_the_kernel_sources(tmp_path, monkeypatch):
         f.write("\n// edit\n")
     assert pt.kernel_source_sha("ring4_256") != ring
     assert pt.kernel_source_sha("gemv_lds") != gemv
+
+
+def test_duration_quantiles():
+    q = pt.duration_quantiles([1000 * i for i in range(1, 11)])   # 1 .. 10 us
+    assert q == {"avg": 5.5, "median": 5.5, "min": 1.0, "p90": 9.0, "max": 10.0}
+    assert pt.duration_quantiles([7000])["p90"] == 7.0

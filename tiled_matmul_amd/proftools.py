@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the committed profiles (host tool, no GPU).
 
     python -m tiled_matmul_amd.proftools stats <kernel_trace.csv> [--skip-first N]
-        per-kernel dispatch count and average / min / max duration (us), optionally without
+        per-kernel dispatch count and average / median / min / p90 / max duration (us), optionally without
         each kernel's first N dispatches (the warm-up launches of a timed run)
     python -m tiled_matmul_amd.proftools traffic --fetch F.csv --write W.csv \
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --kernel SUBSTR \
@@ -77,6 +77,14 @@ def kernel_durations(path):
             start, end = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
             d[name].append((start, end - start))
     return {k: [dur for _, dur in sorted(v)] for k, v in d.items()}
+
+
+def duration_quantiles(ns):
+    """Average, median, min, 90th percentile (nearest rank) and max of durations in ns, in us."""
+    v = sorted(ns)
+    p90 = v[min(len(v) - 1, max(0, -(-9 * len(v) // 10) - 1))]
+    return {"avg": statistics.mean(v) / 1e3, "median": statistics.median(v) / 1e3, "min": v[0] / 1e3,
+            "p90": p90 / 1e3, "max": v[-1] / 1e3}
 
 
 def counter_per_dispatch(path, counter, substr):
@@ -159,10 +167,13 @@ def main():
         print(json.dumps(mfma_summary(a.counters, a.trace, a.kernel, a.peak_tflops)))
         return
     if a.cmd == "stats":
+        print("| Kernel | Calls | Avg (us) | Median (us) | Min (us) | p90 (us) | Max (us) |")
+        print("|---|---|---|---|---|---|---|")
         for name, v in sorted(kernel_durations(a.trace).items(), key=lambda x: -sum(x[1])):
             v = v[a.skip_first:] if len(v) > a.skip_first else v
-            print(f"| {name[:90]} | {len(v)} | {statistics.mean(v) / 1e3:.2f} | "
-                  f"{min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} |")
+            q = duration_quantiles(v)
+            print(f"| {name[:90]} | {len(v)} | {q['avg']:.2f} | {q['median']:.2f} | {q['min']:.2f} | "
+                  f"{q['p90']:.2f} | {q['max']:.2f} |")
         return
     fetch, nf = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
     write, nw = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
