@@ -133,6 +133,12 @@ constexpr int BKV = 64;
 #define TMM_ATTN_QT64 2
 #endif
 
+// attn_mfma_kernel's key loop: one barrier per block, block j+1's loads issued after it (1),
+// or two, block j+1's loads issued before the first (0).
+#ifndef TMM_ATTN_ONE_BARRIER
+#define TMM_ATTN_ONE_BARRIER 1
+#endif
+
 // Wave priority raised over each block's two MFMA phases (1) or left alone (0).
 #ifndef TMM_ATTN_SETPRIO
 #define TMM_ATTN_SETPRIO 1
@@ -279,13 +285,21 @@ __global__ __launch_bounds__(256, QT == 2 ? 2 : 1) void attn_mfma_kernel(AttnArg
     if (nblk > 0) load_block(0, 0);
     for (int j = 0; j < nblk; ++j) {
         const int buf = j & 1;
-        if (j + 1 < nblk) {
-            load_block(j + 1, buf ^ 1);
-            wait_vmcnt<2 * LPT>();   // block j's loads (this wave) have landed
-        } else {
+        if (TMM_ATTN_ONE_BARRIER) {
+            // One barrier per block: after it every wave's loads of block j have landed and
+            // every wave is done with block j-1, whose buffer then takes block j+1.
             wait_vmcnt<0>();
+            barrier();
+            if (j + 1 < nblk) load_block(j + 1, buf ^ 1);
+        } else {
+            if (j + 1 < nblk) {
+                load_block(j + 1, buf ^ 1);
+                wait_vmcnt<2 * LPT>();   // block j's loads (this wave) have landed
+            } else {
+                wait_vmcnt<0>();
+            }
+            barrier();                   // ... and every wave's
         }
-        barrier();                   // ... and every wave's
         const uint8_t* Kt = lds[buf][0];
         const uint8_t* Vt = lds[buf][1];
         const int64_t kv0 = static_cast<int64_t>(j) * BKV;
@@ -413,7 +427,8 @@ __global__ __launch_bounds__(256, QT == 2 ? 2 : 1) void attn_mfma_kernel(AttnArg
         }
         if (TMM_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
         }          // kv0 <= wave_kend
-        barrier();   // every wave is done with buffer `buf` before block j + 2 is loaded into it
+        if (!TMM_ATTN_ONE_BARRIER)
+            barrier();   // every wave is done with buffer `buf` before block j + 2 is loaded into it
     }
 
     // O = O^T / l: lane holds query qw + 16 qt + lq, head-dim 16 dt + 4 lg .. + 3.
