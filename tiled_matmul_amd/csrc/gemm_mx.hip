@@ -15,9 +15,11 @@
 // k = 16 g .. 16 g + 15 and bytes 16-31 are k = 32 + 16 g .. 32 + 16 g + 15 of the 64-deep
 // step, and the scale operand of lane group h applies to k = 32 h .. 32 h + 31.  So a lane
 // reads 16-byte chunks 4 kk + g and 4 kk + 2 + g of its row and passes the scale of 32-block
-// 2 kk + g of the 128-deep block.  The scales are not in LDS (the rings fill it): each lane
-// loads, per fragment and block, the dword that holds its row's four 32-block scales and
-// shifts the byte it needs into place when it reads the fragment.
+// 2 kk + g of the 128-deep block.  The scales are not in LDS (the rings fill it): every lane
+// needs, per fragment and block, the dword that holds its row's four 32-block scales, and
+// shifts the byte it needs into place when it reads the fragment.  The two halves of the wave
+// cover the same 32 rows, so one load fetches two blocks' dwords (the low half block j, the
+// high half block j + 1) and a permlane32 swap gives every lane both.
 //
 // mx_simple_kernel: any K (multiple of 32), pitch and alignment; 64 x 64 tile per workgroup,
 // each thread 4 x 4 outputs, operands decoded with the gfx950 conversion instructions and
@@ -26,6 +28,12 @@
 #include "mfma_step.hpp"
 
 namespace tmm {
+
+// Scale dwords of two consecutive blocks per load (the halves of the wave load one block each,
+// a permlane32 swap shares them): half the scale load instructions.
+#ifndef TMM_MX_SCALE_PAIRS
+#define TMM_MX_SCALE_PAIRS 1
+#endif
 
 // MFMAs at the end of each k step that follow its last fragment read (see step()).
 #ifndef TMM_MX_TAIL
@@ -155,6 +163,34 @@ __global__ __launch_bounds__(256, 1) void mx_ring_kernel(MxArgs g, TileGrid tg, 
             else
                 sa[q - FN] = __builtin_amdgcn_raw_buffer_load_b32(rsa, j < nk ? sa0 + (q - FN) * sstrideA : OOB, soff, 0);
         };
+        // With TMM_MX_SCALE_PAIRS: scale dwords of blocks j (lanes 0-31) and j + 1 (lanes 32-63)
+        // in one load per fragment; swap_scales then gives every lane both (the low half's
+        // values in the first set, the high half's in the second).
+        auto load_scale_pair = [&](int q, int j, int (&sb)[FN], int (&sa)[FM]) {
+            j = __builtin_amdgcn_readfirstlane(j);
+            const int jl = j + (lane >> 5);
+            const uint32_t soff = j < nk ? static_cast<uint32_t>(j) * 4u : 0u;
+            const uint32_t hi = static_cast<uint32_t>(lane >> 5) * 4u;
+            if (q < FN)
+                sb[q] = __builtin_amdgcn_raw_buffer_load_b32(rsb, jl < nk ? sb0 + q * sstrideB + hi : OOB, soff, 0);
+            else
+                sa[q - FN] = __builtin_amdgcn_raw_buffer_load_b32(rsa, jl < nk ? sa0 + (q - FN) * sstrideA + hi : OOB,
+                                                                  soff, 0);
+        };
+        auto swap_scales = [&](int (&sb0_)[FN], int (&sa0_)[FM], int (&sb1_)[FN], int (&sa1_)[FM]) {
+#pragma unroll
+            for (int q = 0; q < FN; ++q) {
+                const auto r = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(sb0_[q]),
+                                                                static_cast<uint32_t>(sb0_[q]), false, false);
+                sb0_[q] = static_cast<int>(r[0]), sb1_[q] = static_cast<int>(r[1]);
+            }
+#pragma unroll
+            for (int q = 0; q < FM; ++q) {
+                const auto r = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(sa0_[q]),
+                                                                static_cast<uint32_t>(sa0_[q]), false, false);
+                sa0_[q] = static_cast<int>(r[0]), sa1_[q] = static_cast<int>(r[1]);
+            }
+        };
         using F = MxFrags<FN, FM>;
         // Read q of k step kk (q / 2: fragment, B first; q % 2: which 16 bytes); with the first
         // read the fragment takes scale byte 2 kk + lg of its set entry.
@@ -184,15 +220,22 @@ __global__ __launch_bounds__(256, 1) void mx_ring_kernel(MxArgs g, TileGrid tg, 
         // Prologue: scales(0), A(0), B(0), scales(1), A(1), B(1), in this order (fenced: the
         // wait counts on it); all but A(1), B(1) complete.
 #pragma unroll
-        for (int q = 0; q < FN + FM; ++q) load_scales(q, 0, sbX, saX);
+        for (int q = 0; q < FN + FM; ++q) {
+            if (TMM_MX_SCALE_PAIRS)
+                load_scale_pair(q, 0, sbX, saX);
+            else
+                load_scales(q, 0, sbX, saX);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < L; ++q) load_one(true, q, 0, 0);
 #pragma unroll
         for (int q = 0; q < L; ++q) load_one(false, q, 0, B_BASE);
         __builtin_amdgcn_sched_barrier(0);
+        if (!TMM_MX_SCALE_PAIRS) {
 #pragma unroll
-        for (int q = 0; q < FN + FM; ++q) load_scales(q, 1, sbY, saY);
+            for (int q = 0; q < FN + FM; ++q) load_scales(q, 1, sbY, saY);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < L; ++q) load_one(true, q, 1, TILE);
@@ -201,6 +244,7 @@ __global__ __launch_bounds__(256, 1) void mx_ring_kernel(MxArgs g, TileGrid tg, 
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<2 * L>();
         barrier();
+        if (TMM_MX_SCALE_PAIRS) swap_scales(sbX, saX, sbY, saY);
         F f[2];
 #pragma unroll
         for (int q = 0; q < NR; ++q) read_one(f[0], q, 0, B_BASE, 0, sbX, saX);
@@ -208,19 +252,29 @@ __global__ __launch_bounds__(256, 1) void mx_ring_kernel(MxArgs g, TileGrid tg, 
 
         int a0 = 0, a1 = TILE, a2 = 2 * TILE, b0 = B_BASE, b1 = B_BASE + TILE;
         // One iteration on block b with its scales in (sbC, saC) and block b+1's in (sbN, saN).
-        auto iteration = [&](int b, int (&sbC)[FN], int (&saC)[FM], int (&sbN)[FN], int (&saN)[FM]) {
+        // With scale pairs, an even iteration loads the pair (b+2, b+3) into block b's set and
+        // the next (odd) one swaps it into the sets of blocks b+2 and b+3 once both are free.
+        auto iteration = [&](auto odd, int b, int (&sbC)[FN], int (&saC)[FM], int (&sbN)[FN], int (&saN)[FM]) {
+            constexpr bool ODD = decltype(odd)::value;
             step<FN, FM, NR, L, true, MM, TMM_MX_TAIL>(acc, f[0], [&](int q) { read_one(f[1], q, a0, b0, 1, sbC, saC); },
                                              [&](int q) { load_one(true, q, b + 2, a2); });
             wait_cnt<L, 0>();   // all but this step's A(b+2) loads: B(b+1), scales(b+1) landed
             barrier();
-            step<FN, FM, NR, L + FN + FM, true, MM, TMM_MX_TAIL>(
+            constexpr bool PAIRS = TMM_MX_SCALE_PAIRS != 0;
+            if constexpr (PAIRS && ODD) swap_scales(sbN, saN, sbC, saC);
+            constexpr int NS = PAIRS && ODD ? 0 : FN + FM;   // scale loads in this step
+            step<FN, FM, NR, L + NS, true, MM, TMM_MX_TAIL>(
                 acc, f[1], [&](int q) { read_one(f[0], q, a1, b1, 0, sbN, saN); },
                 [&](int q) {
                     // scales first: a wait LLVM places for them then leaves the B loads in flight
-                    if (q < FN + FM)
-                        load_scales(q, b + 2, sbC, saC);
-                    else
-                        load_one(false, q - (FN + FM), b + 2, b0);
+                    if (q < NS) {
+                        if constexpr (PAIRS)
+                            load_scale_pair(q, b + 2, sbC, saC);
+                        else
+                            load_scales(q, b + 2, sbC, saC);
+                    } else {
+                        load_one(false, q - NS, b + 2, b0);
+                    }
                 });
             __builtin_amdgcn_sched_barrier(0);
             wait_cnt<63, 0>();
@@ -235,9 +289,9 @@ __global__ __launch_bounds__(256, 1) void mx_ring_kernel(MxArgs g, TileGrid tg, 
         // path from one even iteration straight to the next, LLVM waits for loads in flight
         // before every scale read of step 0).  nk >= 1.
         for (int b = 0;; b += 2) {
-            iteration(b, sbX, saX, sbY, saY);
+            iteration(std::integral_constant<bool, false>{}, b, sbX, saX, sbY, saY);
             if (b + 1 >= nk) break;
-            iteration(b + 1, sbY, saY, sbX, saX);
+            iteration(std::integral_constant<bool, true>{}, b + 1, sbY, saY, sbX, saX);
             if (b + 2 >= nk) break;
         }
         wait_vmcnt<0>();   // the trailing zero-fill loads have landed
