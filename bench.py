@@ -12,8 +12,9 @@ after idle: back-to-back 4096^3 GEMMs take ~144-149 us each over the first 100 l
 ~108-110 us over the next 100 and ~104 us from then on, so a short warm-up times part of that
 transient.  The default K = 5000 (about 0.5 s at 4096^3) is long enough for the driver's clock
 reading, sampled during the timed steps, to be reported (from 0.4 s of timed steps on:
-`sclk_mhz`, and the rate against the peak scaled to that clock, `roofline.frac_at_sclk`).  Inputs rotate over several buffer sets whose total
-exceeds the 256 MB Infinity Cache, so no step finds its operands in a cache left warm by
+`sclk_mhz`, and the rate against the peak scaled to that clock, `roofline.frac_at_sclk`).
+Inputs rotate over several buffer sets whose total exceeds the 256 MB Infinity Cache, so no
+step finds its operands in a cache left warm by
 the previous one.  The GEMV leg captures its launches in a HIP graph (one kernel is a few
 microseconds, below the Python launch overhead) and times graph replays.
 
