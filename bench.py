@@ -14,9 +14,9 @@ transient.  The default K = 5000 (about 0.5 s at 4096^3) is long enough for the 
 reading, sampled during the timed steps, to be reported (from 0.4 s of timed steps on:
 `sclk_mhz`, and the rate against the peak scaled to that clock, `roofline.frac_at_sclk`).
 Inputs rotate over several buffer sets whose total exceeds the 256 MB Infinity Cache, so no
-step finds its operands in a cache left warm by
-the previous one.  The GEMV leg captures its launches in a HIP graph (one kernel is a few
-microseconds, below the Python launch overhead) and times graph replays.
+step finds its operands in a cache left warm by the previous one.  The GEMV leg captures its
+launches in a HIP graph (one kernel is a few microseconds, below the Python launch overhead)
+and times graph replays.
 
 cpu_baseline: the CPU oracle (plain fp64 triple loop, OpenMP over rows) timed on a bounded
 sample of the same workload: a band of rows of C, all N columns, the full K.  Its rows are
