@@ -27,3 +27,24 @@ def test_sclk_sampler_without_sysfs():
     with s:
         pass
     assert s.summary() is None
+
+
+def test_traffic_taken_only_on_the_same_sources_and_launch(tmp_path, monkeypatch):
+    import json
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    sha = bench.kernel_source_sha("ring4_256")
+    def put(kernel, wl, **kw):
+        d = {"kernel_source_sha": sha if kernel != "splitk_reduce" else bench.kernel_source_sha(kernel),
+             "hbm_bytes_per_launch": 100.0}
+        d.update(kw)
+        json.dump(d, open(tmp_path / "profiles" / f"traffic_{kernel}_{wl}.json", "w"))
+    put("ring4_256", "w1", grid=256, block=256)
+    assert bench.traffic_for("ring4_256", "w1", 256, 256) == 100.0
+    assert bench.traffic_for("ring4_256", "w1", 240, 256) is None          # another launch
+    assert bench.traffic_for("ring4_256", "w2", 256, 256) is None          # no summary
+    put("ring4_256", "w3", grid=256, block=256, kernel_source_sha="0" * 16)
+    assert bench.traffic_for("ring4_256", "w3", 256, 256) is None          # other sources
+    put("ring4_256", "w4", grid=256, block=256)
+    put("splitk_reduce", "w4")
+    assert bench.traffic_for("ring4_256+splitk_reduce", "w4", 256, 256) == 200.0   # a two-kernel call
