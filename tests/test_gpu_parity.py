@@ -127,6 +127,22 @@ def test_padded_pitches(variant):
     assert_exact(got, A, B, K, OUT_FP32, what="padded pitches")
 
 
+# The skinny-M path (dot-product form for M <= 4, MFMA form above) with padded pitches whose
+# padding holds NaN: K = 4360 spans two 4096-deep phases and ends mid 512-element chunk, so any
+# read past K in W or X, or a wrong pitch, shows.
+@pytest.mark.parametrize("variant", [V.GEMM_VARIANT_GEMV, V.GEMM_VARIANT_AUTO])
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+def test_gemv_padded_pitches(variant, M):
+    N, K = 70, 4360
+    A = synth.integers(M, K, 61 + M, ld=K + 24)
+    B = synth.integers(N, K, 62 + M, ld=K + 8)
+    for out_dtype in (OUT_FP32, OUT_BF16):
+        got = run_gemm(A, B, K, out_dtype, variant=variant, ldc=N + 3)
+        assert_exact(got, A, B, K, out_dtype, what=f"gemv padded pitches M={M}")
+    rc, name, _, _ = tm.gemm_bf16_plan(variant, 1, M, N, K, 16, K + 24, 0, 16, K + 8, 0, 16, N + 3, 0, 0)
+    assert rc == 0 and name == ("gemv_lds" if M <= 4 else "gemv")
+
+
 # Ragged K (not a multiple of 8) and rows that are only 4- or 8-byte aligned: the pipelined
 # kernels load whole 16-byte chunks below K rounded down to 8 and add the rest in one extra
 # k step.  Pitch padding holds NaN, so a tail element read from beyond K would show.
