@@ -10,7 +10,7 @@ timed with HIP events recorded on the stream the kernels are launched on (the li
 launches on torch's current stream).  The default W = 300 covers the engine clock's settling
 after idle: back-to-back 4096^3 GEMMs take ~144-149 us each over the first 100 launches,
 ~108-110 us over the next 100 and ~104 us from then on, so a short warm-up times part of that
-transient.  The default K = 5000 (about 0.5 s at 4096^3) is long enough for the driver's clock
+transient.  The default K = 5000 (about 0.5 s at 4096^3) is long enough for the amdgpu driver's clock
 reading, sampled during the timed steps, to be reported (from 0.4 s of timed steps on:
 `sclk_mhz`, and the rate against the peak scaled to that clock, `roofline.frac_at_sclk`).
 Inputs rotate over several buffer sets whose total exceeds the 256 MB Infinity Cache, so no
@@ -22,8 +22,8 @@ cpu_baseline: the CPU oracle (plain fp64 triple loop, OpenMP over rows) timed on
 sample of the same workload: a band of rows of C, all N columns, the full K.  Its rows are
 also compared with the GPU output under the acceptance bound.
 
-Prints ONE JSON line.  `python bench.py --gpus N` with N > 1 exits: this build measures
-one GPU.
+Prints ONE JSON line.  `python bench.py --gpus N` with N > 1 exits with status 2: the
+bench measures one GPU.
 """
 from __future__ import annotations
 
@@ -87,7 +87,7 @@ def make_sets(name, torch, min_bytes, la=0, lb=0):
 
 
 class SclkSampler:
-    """The engine clock the driver reports (the level marked current in pp_dpm_sclk), read
+    """The engine clock the amdgpu driver reports (the level marked current in pp_dpm_sclk), read
     from sysfs every 2 ms by a host thread while the timed steps run; no GPU call."""
 
     def __init__(self):
@@ -121,7 +121,7 @@ class SclkSampler:
             self._stop.set()
             self._t.join()
 
-    # The driver's reading trails the clock (a short run reads partly the idle or warm-up clock
+    # The amdgpu driver's reading trails the clock (a short run reads partly the idle or warm-up clock
     # before it), so it is reported only for timed regions at least this long.
     MIN_WALL_S = 0.4
 
@@ -132,7 +132,7 @@ class SclkSampler:
             return None
         v = sorted(self.mhz)
         return {"median": v[len(v) // 2], "mean": round(sum(v) / len(v), 1), "min": v[0], "max": v[-1],
-                "samples": len(v), "source": "pp_dpm_sclk (driver's current level), sampled every 2 ms"}
+                "samples": len(v), "source": "pp_dpm_sclk (the amdgpu driver's current level), sampled every 2 ms"}
 
 
 def time_steps(launch, nsets, steps, warmup, torch, sampler=None, chunk=0):
@@ -350,7 +350,7 @@ def gemm_roofline(res):
         r = {"bound": "mfma", "achieved": res["tflops"], "peak": MFMA_TFLOPS, "unit": "TFLOP/s",
              "frac": res["tflops"] / MFMA_TFLOPS}
     if bound == "mfma" and res.get("sclk"):
-        # the same rate against the dense peak scaled to the clock the driver reported
+        # the same rate against the dense peak scaled to the clock the amdgpu driver reported
         r["frac_at_sclk"] = res["tflops"] / (MFMA_TFLOPS * res["sclk"]["median"] / 2400.0)
     r.update({"traffic": traffic_for(res["kernel"], res["name"], res["grid"], res["block"]),
               "flops_per_launch": res["flops"], "algorithmic_bytes_per_launch": res["bytes"],
@@ -494,8 +494,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the GEMM shards by columns of B with no communication; see the design notes)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (each GPU would "
+              "take its own columns of B and C, with no communication between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -1,4 +1,4 @@
-"""Host-side pieces of bench.py (no GPU): the engine-clock sampler reads the level the driver
+"""Host-side pieces of bench.py (no GPU): the engine-clock sampler reads the level the amdgpu driver
 marks current in pp_dpm_sclk."""
 import os
 import sys
@@ -18,7 +18,7 @@ def test_sclk_sampler_reads_the_current_level(tmp_path):
     r = s.summary()
     assert r["median"] == 1897 and r["min"] == 1897 and r["max"] == 1897 and r["samples"] >= 1
     assert s.summary(wall_s=0.45)["median"] == 1897
-    assert s.summary(wall_s=0.1) is None          # too short for the driver's reading
+    assert s.summary(wall_s=0.1) is None          # too short for the amdgpu driver's reading
 
 
 def test_sclk_sampler_without_sysfs():
