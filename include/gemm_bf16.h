@@ -197,9 +197,13 @@ int gemm_bf16_layout_plan(int a_layout, int b_layout, int variant, int64_t batch
  * The result is deterministic (the same bits on every run with the same S) and differs from
  * gemm_bf16_layout only in the order of the fp32 additions.
  *   splits           S >= 1 to force (capped at the number of K blocks, ceil(K / 64)), or 0
- *                    to let the library choose: S = 1 when the 256 x 256 tiles already
- *                    fill 90 % of the compute units, else the most ranges that fill them
- *                    (at least 4 K blocks per range) and fit in the workspace.
+ *                    to let the library choose.  Automatic S: 1 unless the call would run
+ *                    a tiled MFMA kernel (not the skinny-M path) whose tiles cover at most
+ *                    half of the compute units; then S = min(CUs / T, floor(nk / 8),
+ *                    floor(workspace_bytes / (batch * M * N * 4))), at least 1, where T is
+ *                    the number of 256 x 256 tiles (batch included) and nk = ceil(K / 64):
+ *                    one work item per compute unit, at least 8 K blocks per range, and no
+ *                    more ranges than the workspace holds.
  *   workspace        device memory owned by the caller, 16-byte aligned, at least
  *                    S * batch * M * N * 4 bytes (see gemm_bf16_splitk_plan for S); only
  *                    used, and may be NULL, when S == 1.  Its contents on entry do not

@@ -66,10 +66,16 @@ def attention(Q, K, V, scale: float, causal: bool, heads=None, rows=None):
         O[n] = P @ V[b, g]
         PV[n] = P @ np.abs(V[b, g])
         LSE[n] = np.where(ok, m[:, 0] + np.log(np.where(ok, l[:, 0], 1.0)), -np.inf)
-        # scale * max_j sum_c |Q_ic K_jc| and max_j |S_ij| (allowed j): the score magnitudes
-        # the fp32 error of a score is bounded by
-        Sa = abs(scale) * (np.abs(Q[b, h, rows]) @ np.abs(K[b, g]).T)
-        if causal:
-            Sa = np.where(allowed, Sa, 0.0)
-        SMAG[n] = d * Sa.max(axis=1, initial=0.0) + np.where(np.isfinite(S), np.abs(S), 0.0).max(axis=1, initial=0.0)
+        SMAG[n] = score_magnitude(Q[b, h, rows], K[b, g], S, scale, allowed if causal else None)
     return O, LSE, PV, SMAG
+
+
+def score_magnitude(Qr, Kg, S, scale: float, allowed=None) -> np.ndarray:
+    """SMAG of each query row: d |scale| max_j sum_c |Q_ic K_jc| + max_j |S_ij| over the
+    allowed keys j (0 for a row with none): the score magnitudes that the fp32 error of a
+    score, accumulated over d products and then scaled, is bounded by."""
+    d = Qr.shape[-1]
+    Sa = abs(scale) * (np.abs(Qr) @ np.abs(Kg).T)
+    if allowed is not None:
+        Sa = np.where(allowed, Sa, 0.0)
+    return d * Sa.max(axis=1, initial=0.0) + np.where(np.isfinite(S), np.abs(S), 0.0).max(axis=1, initial=0.0)

@@ -86,7 +86,15 @@ def gemm(A, SA, B, SB, fa: int, fb: int, K: int | None = None, rows=None):
     b = scaled(B, SB, fb, K)
     C = a @ b.T
     Mag = np.abs(a) @ np.abs(b).T
-    ea = np.where(a != 0, np.exp2(exponent_field(A[:, :K], fa)) * np.repeat(decode_scale(SA[:, :K // 32]), 32, axis=1), 0.0)
-    eb = np.where(b != 0, np.exp2(exponent_field(B[:, :K], fb)) * np.repeat(decode_scale(SB[:, :K // 32]), 32, axis=1), 0.0)
-    F = ea @ eb.T
+    F = exponent_magnitudes(A, SA, fa, K) @ exponent_magnitudes(B, SB, fb, K).T
     return C, Mag, F
+
+
+def exponent_magnitudes(codes, scales, fmt: int, K: int) -> np.ndarray:
+    """Per element of the first K columns: 2^(e + s - 127) (e: the element's unbiased
+    exponent field, s: its 32-block's scale code), or 0 for a zero element.  The product of
+    two rows of these, summed over k, is F."""
+    codes = np.asarray(codes)[:, :K]
+    v = decode(codes, fmt)
+    s = np.repeat(decode_scale(np.asarray(scales)[:, :K // 32]), 32, axis=1)
+    return np.where(v != 0, np.exp2(exponent_field(codes, fmt)) * s, 0.0)

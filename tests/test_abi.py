@@ -216,6 +216,11 @@ def test_splitk_plan():
     # at least 8 K blocks per range: K = 1024 (16 blocks) -> 2 ranges
     assert splan(0, K=1024)[:2] == (0, 2)
     assert splan(0, K=960)[:3] == (0, 1, "persist_128")
+    # the threshold: split only while the unsplit kernel's tiles cover at most half the CUs
+    # (128 tiles of 128 x 128 -> S = min(256 / 32 tiles of 256 x 256, 64 blocks / 8) = 8;
+    # 144 tiles -> unsplit)
+    assert splan(0, M=1024, N=2048, K=4096) == (0, 8, "ring4_256", 256)
+    assert splan(0, M=1152, N=2048, K=4096)[:3] == (0, 1, "persist_128")
     # enough tiles already (4096^2: 256 tiles; 64 items of 256 x 256: 256 tiles of 128 x 128):
     # one range
     assert splan(0, M=4096, N=4096, K=4096) == (0, 1, "ring4_256", 256)

@@ -127,3 +127,63 @@ def test_checker_accepts_rounding_and_rejects_an_off_by_one_mask():
     # Lk + 1 keys, bottom-right aligned: row i sees keys 0 .. i + 1
     r = ck.check_attention(Ow.astype(np.float32), O, PV, SM, 64, ck.OUT_FP32)
     assert not r["ok"]
+
+
+# --- SMAG, the score magnitude the attention tolerance is written in -------------------------
+
+def brute_smag(Q, K, scale, causal):
+    """SMAG[b][h][i] = d |scale| max_j sum_c |Q_ic K_jc| + max_j |scale sum_c Q_ic K_jc| over
+    the allowed keys j, with exactly rounded sums (pure-Python loops)."""
+    q, k = att.bf16_to_f64(Q), att.bf16_to_f64(K)
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    out = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in range(Lq):
+                js = [j for j in range(Lk) if not causal or j <= i + Lk - Lq]
+                if not js:
+                    continue
+                mag = max(math.fsum(abs(q[b, h, i, c] * k[b, g, j, c]) for c in range(d)) for j in js)
+                s = max(abs(math.fsum(q[b, h, i, c] * k[b, g, j, c] for c in range(d))) for j in js)
+                out[b, h, i] = d * abs(scale) * mag + abs(scale) * s
+    return out
+
+
+@pytest.mark.parametrize("causal,Lq,Lk", [(False, 5, 7), (True, 6, 4), (True, 5, 5)])
+def test_smag_equals_its_definition(causal, Lq, Lk):
+    Q, K, V = qkv(1, 4, 2, Lq, Lk, 8, 930 + Lq)
+    _, _, _, SMAG = att.attention(Q, K, V, -0.3, causal)
+    ref = brute_smag(Q, K, -0.3, causal).reshape(SMAG.shape)
+    assert np.allclose(SMAG, ref, rtol=2.0 ** -45, atol=0.0)
+
+
+def test_smag_pin_rejects_planted_mistakes(monkeypatch):
+    """The pin above fails on plausible mistakes planted in the oracle: the d factor dropped,
+    the scale's sign kept (negative scale), masked keys counted."""
+    Q, K, V = qkv(1, 2, 1, 6, 4, 8, 940)
+    scale = -0.3
+    ref = brute_smag(Q, K, scale, True).reshape(2, 6)
+    good = att.score_magnitude
+
+    def variant(Qr, Kg, S, scale, allowed, factor):
+        Sa = scale * (np.abs(Qr) @ np.abs(Kg).T)
+        if allowed is not None:
+            Sa = np.where(allowed, Sa, 0.0)
+        return factor * Sa.max(axis=1, initial=0.0) + np.where(np.isfinite(S), np.abs(S), 0.0).max(axis=1, initial=0.0)
+
+    def no_d(Qr, Kg, S, scale, allowed=None):
+        return variant(Qr, Kg, S, abs(scale), allowed, 1)
+
+    def signed_scale(Qr, Kg, S, scale, allowed=None):
+        return variant(Qr, Kg, S, scale, allowed, Qr.shape[-1])
+
+    def mask_ignored(Qr, Kg, S, scale, allowed=None):
+        return good(Qr, Kg, S, scale, None)
+
+    for mutant in (no_d, signed_scale, mask_ignored):
+        monkeypatch.setattr(att, "score_magnitude", mutant)
+        _, _, _, SMAG = att.attention(Q, K, V, scale, True)
+        assert not np.allclose(SMAG, ref, rtol=2.0 ** -45, atol=0.0), mutant.__name__
+    monkeypatch.setattr(att, "score_magnitude", good)
