@@ -7,16 +7,21 @@ is the square 4096^3 GEMM (bf16 inputs N(0,1), fp32 output); the decode GEMV
 
 Timing: W untimed warm-up steps, then K steps between two torch.cuda.synchronize() calls,
 timed with HIP events recorded on the stream the kernels are launched on (the library
-launches on torch's current stream).  The default W = 300 covers the engine clock's settling
-after idle: back-to-back 4096^3 GEMMs take ~144-149 us each over the first 100 launches,
-~108-110 us over the next 100 and ~104 us from then on, so a short warm-up times part of that
-transient.  The default K = 5000 (about 0.5 s at 4096^3) is long enough for the amdgpu driver's clock
-reading, sampled during the timed steps, to be reported (from 0.4 s of timed steps on:
-`sclk_mhz`, and the rate against the peak scaled to that clock, `roofline.frac_at_sclk`).
-Inputs rotate over several buffer sets whose total exceeds the 256 MB Infinity Cache, so no
-step finds its operands in a cache left warm by the previous one.  The GEMV leg captures its
+launches on torch's current stream).  The engine clock is not steady over a short run: from
+idle, back-to-back 4096^3 GEMMs run ~104-108 us each for the first ~2 ms, then the clock drops
+and they take ~113-128 us for a while, and only after many milliseconds settle near ~104 us.
+A run of 5 warm-up and 20 timed steps therefore averages across that drop; the defaults
+(300 warm-up, 5000 timed steps) time the settled state.  The amdgpu driver's clock reading is
+sampled at the start and end of the timed region and every 2 ms in between (`sclk_mhz`;
+in a region of a few milliseconds it mostly shows the clock of what ran before).  Inputs
+rotate over several buffer sets whose total exceeds the 256 MB Infinity Cache, so no step
+finds its operands in a cache left warm by the previous one.  The GEMV leg captures its
 launches in a HIP graph (one kernel is a few microseconds, below the Python launch overhead)
-and times graph replays.
+and times graph replays; beside it, the same way, a plain streaming read of the same 32 MiB
+buffers and an empty kernel (libtmm_ceiling.so) measure what any single launch can reach on
+those bytes (`gemv.ceiling`).  Where a rocprofv3 kernel-trace summary of the same kernel,
+sources and launch is committed under profiles/, `roofline.trace` gives the rates its traced
+durations imply.
 
 cpu_baseline: the CPU oracle (plain fp64 triple loop, OpenMP over rows) timed on a bounded
 sample of the same workload: a band of rows of C, all N columns, the full K.  Its rows are
@@ -87,30 +92,36 @@ def make_sets(name, torch, min_bytes, la=0, lb=0):
 
 
 class SclkSampler:
-    """The engine clock the amdgpu driver reports (the level marked current in pp_dpm_sclk), read
-    from sysfs every 2 ms by a host thread while the timed steps run; no GPU call."""
+    """The engine clock the amdgpu driver reports (the level marked current in pp_dpm_sclk): one
+    reading as the timed region starts, one as it ends (after the final synchronize), and
+    readings every 2 ms in between from a host thread; no GPU call."""
 
     def __init__(self):
         import glob
         paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
         self.path = paths[0] if paths else None
         self.mhz = []
+        self.start = self.end = None
+
+    def read(self):
+        import re
+        try:
+            with open(self.path) as f:
+                m = re.search(r"(\d+)\s*[Mm]hz\s*\*", f.read())
+            return int(m.group(1)) if m else None
+        except OSError:
+            return None
 
     def _run(self):
-        import re
-        while not self._stop.is_set():
-            try:
-                with open(self.path) as f:
-                    m = re.search(r"(\d+)\s*[Mm]hz\s*\*", f.read())
-                if m:
-                    self.mhz.append(int(m.group(1)))
-            except OSError:
-                return
-            self._stop.wait(0.002)
+        while not self._stop.wait(0.002):
+            v = self.read()
+            if v is not None:
+                self.mhz.append(v)
 
     def __enter__(self):
         import threading
         if self.path:
+            self.start = self.read()
             self._stop = threading.Event()
             self._t = threading.Thread(target=self._run, daemon=True)
             self._t.start()
@@ -120,19 +131,20 @@ class SclkSampler:
         if self.path:
             self._stop.set()
             self._t.join()
-
-    # The amdgpu driver's reading trails the clock (a short run reads partly the idle or warm-up clock
-    # before it), so it is reported only for timed regions at least this long.
-    MIN_WALL_S = 0.4
+            self.end = self.read()
 
     def summary(self, wall_s=None):
-        """Median and mean MHz over the samples, or None where sysfs does not expose it or the
-        timed region was shorter than MIN_WALL_S."""
-        if not self.mhz or (wall_s is not None and wall_s < self.MIN_WALL_S):
+        """Median, mean, min and max MHz over every reading (start and end included), or None
+        where sysfs does not expose the clock.  The driver's reading trails the clock, so in a
+        region of a few milliseconds it mostly shows the clock of what ran just before."""
+        v = sorted(x for x in [self.start, *self.mhz, self.end] if x is not None)
+        if not v:
             return None
-        v = sorted(self.mhz)
         return {"median": v[len(v) // 2], "mean": round(sum(v) / len(v), 1), "min": v[0], "max": v[-1],
-                "samples": len(v), "source": "pp_dpm_sclk (the amdgpu driver's current level), sampled every 2 ms"}
+                "start": self.start, "end": self.end, "samples": len(v),
+                "timed_region_s": None if wall_s is None else round(wall_s, 4),
+                "source": "pp_dpm_sclk (the amdgpu driver's current level): at the start and end of the "
+                          "timed region and every 2 ms in between"}
 
 
 def time_steps(launch, nsets, steps, warmup, torch, sampler=None, chunk=0):
@@ -179,6 +191,35 @@ def traffic_for(kernel, workload, grid=None, block=None):
             return None
         total += t.get("hbm_bytes_per_launch")
     return total
+
+
+def trace_for(kernel, workload, grid=None, block=None):
+    """The committed rocprofv3 kernel-trace summary of this kernel on this workload
+    (profiles/trace_<kernel>_<workload>.json), if it was taken on the current sources of the
+    kernel and the same launch shape; else None."""
+    path = os.path.join(ROOT, "profiles", f"trace_{kernel}_{workload}.json")
+    if "+" in kernel or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha(kernel):
+        return None
+    if t.get("grid") is not None and (t.get("grid"), t.get("block")) != (grid, block):
+        return None
+    t["source"] = os.path.relpath(path, ROOT)
+    return t
+
+
+def traced_rate(t, work, peak, unit_scale):
+    """Rates from a trace summary: `work` (FLOPs or bytes) per launch over its average and
+    median durations, scaled by unit_scale, and their fractions of `peak`."""
+    if t is None:
+        return None
+    avg = work / (t["avg_us"] * 1e-6) / unit_scale
+    med = work / (t["median_us"] * 1e-6) / unit_scale
+    return {"avg_us": t["avg_us"], "median_us": t["median_us"], "achieved_avg": avg,
+            "achieved_median": med, "frac_avg": avg / peak, "frac_median": med / peak,
+            "dispatches": t["dispatches"], "command": t["command"], "source": t["source"]}
 
 
 def gemm_leg(args, torch):
@@ -352,6 +393,11 @@ def gemm_roofline(res):
     if bound == "mfma" and res.get("sclk"):
         # the same rate against the dense peak scaled to the clock the amdgpu driver reported
         r["frac_at_sclk"] = res["tflops"] / (MFMA_TFLOPS * res["sclk"]["median"] / 2400.0)
+    tr = trace_for(res["kernel"], res["name"], res["grid"], res["block"])
+    if bound == "hbm":
+        r["trace"] = traced_rate(tr, res["bytes"], HBM_TB_S * 1e3, 1e9)
+    else:
+        r["trace"] = traced_rate(tr, res["flops"], MFMA_TFLOPS, 1e12)
     r.update({"traffic": traffic_for(res["kernel"], res["name"], res["grid"], res["block"]),
               "flops_per_launch": res["flops"], "algorithmic_bytes_per_launch": res["bytes"],
               "intensity_flop_per_byte": ai})
@@ -373,26 +419,17 @@ def gemv_leg(args, torch, name="gemv_m1"):
         launch(i)
     torch.cuda.synchronize()
     reps = max(1, args.gemv_launches // n)
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    with torch.cuda.graph(g, stream=s):
-        for r in range(reps):
-            for i in range(n):
-                launch(i)
-    g.replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.gemv_replays):
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
     launches = reps * n * args.gemv_replays
-    us = start.elapsed_time(end) * 1e3 / launches
+    us = graph_time_us(torch, launch, n, reps, args.gemv_replays)
     nbytes = rl.algorithmic_bytes(M, N, K, 4 if out == tm.GEMM_OUT_FP32 else 2)
     gbs = nbytes / (us * 1e-6) / 1e9
     _, kname, grid, block = tm.gemm_bf16_plan(0, 1, M, N, K, sets[0][0], K, 0, sets[0][1], K, 0,
                                               sets[0][2], N, 0, out)
+    ceiling = None if args.no_ceiling else ceiling_leg(args, torch, [b for _, b, _ in sets])
+    if ceiling is not None:
+        # the same comparison on equal footing: the GEMV's algorithmic bytes per second against
+        # the plain read's bytes per second
+        ceiling["gemv_frac_of_stream_read"] = gbs / ceiling["stream_read"]["gbs"]
     return {
         "metric": f"GB/s and % of HBM peak, decode GEMV M={M} N={N} K={K} (bf16 in, "
                   f"{'fp32' if out == tm.GEMM_OUT_FP32 else 'bf16'} out)",
@@ -402,8 +439,60 @@ def gemv_leg(args, torch, name="gemv_m1"):
         "timing": "HIP events around replays of a captured HIP graph of back-to-back launches",
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_TB_S * 1e3, "unit": "GB/s",
                      "frac": gbs / (HBM_TB_S * 1e3), "traffic": traffic_for(kname, name, grid, block),
-                     "algorithmic_bytes_per_launch": nbytes},
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "trace": traced_rate(trace_for(kname, name, grid, block), nbytes, HBM_TB_S * 1e3, 1e9)},
+        "ceiling": ceiling,
     }
+
+
+def graph_time_us(torch, launch, n, reps, replays):
+    """us per launch of `launch(i)` for i over range(n), repeated reps times, captured in one
+    HIP graph and replayed `replays` times between two events (after one untimed replay)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(reps):
+            for i in range(n):
+                launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / (reps * n * replays)
+
+
+def ceiling_leg(args, torch, bufs):
+    """What one launch can reach on the GEMV's bytes: the best cold streaming read of one
+    32 MiB buffer (rotating over the same buffers the GEMV's weights live in, more than twice
+    the Infinity Cache) over a few launch shapes, and the cost of an empty launch; both timed
+    like the GEMV, as back-to-back launches replayed from a HIP graph."""
+    from tiled_matmul_amd import ceiling as cl
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    n = len(bufs)
+    reps = max(1, args.gemv_launches // n)
+    sink = torch.zeros(2048 * 1024 // 64, dtype=torch.float32, device="cuda")
+    shapes = {}
+    for grid in (256, 512, 1024, 2048):
+        for block in (256, 1024):
+            us = graph_time_us(torch, lambda i: cl.stream_read(bufs[i], nbytes, sink, grid, block), n, reps,
+                               args.gemv_replays)
+            shapes[f"{grid}x{block}"] = round(us, 3)
+    best = min(shapes, key=shapes.get)
+    floor = {}
+    for grid, block in ((1, 64), (256, 1024)):
+        floor[f"{grid}x{block}"] = round(graph_time_us(torch, lambda i: cl.launch_floor(grid, block), n, reps,
+                                                       args.gemv_replays), 3)
+    us = shapes[best]
+    return {"stream_read": {"bytes": nbytes, "us": us, "gbs": nbytes / (us * 1e-6) / 1e9,
+                            "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / (HBM_TB_S * 1e3),
+                            "best_launch": best, "us_by_launch": shapes,
+                            "kernel": "ceiling_stream_read (16-byte non-temporal loads, 4 in flight per thread)"},
+            "launch_floor_us": floor,
+            "timing": "HIP events around replays of a captured HIP graph of back-to-back launches"}
 
 
 def cpu_baseline_leg(res, args, torch):
@@ -423,7 +512,9 @@ def cpu_baseline_leg(res, args, torch):
     C_ref, Mag = oracle.gemm(A, B, rows=sel, nthreads=threads)
     t = time.perf_counter() - t0
     flops = 2.0 * rows * N * K
-    out = res["sets"][(args.warmup + args.steps - 1) % len(res["sets"])][2]
+    # time_steps launches set i % nsets for timed step i, so the last timed launch used this set
+    assert args.steps >= 1
+    out = res["sets"][(args.steps - 1) % len(res["sets"])][2]
     if res["batch"] > 1:
         out = out[0]          # the sample is drawn from batch item 0
     got = out[:rows].cpu()
@@ -439,8 +530,18 @@ def cpu_baseline_leg(res, args, torch):
                     break
     except OSError:
         pass
+    single = {}
+    for name in ("single_tile_128", "gemv_m1"):
+        w = synth.WORKLOADS[name]
+        a1, b1 = synth.make_operands(name)
+        t0 = time.perf_counter()
+        oracle.gemm(a1, b1, nthreads=1)
+        dt = time.perf_counter() - t0
+        single[name] = {"seconds": dt, "tflops": 2.0 * w["M"] * w["N"] * w["K"] / dt / 1e12,
+                        "shape": f"{w['M']}x{w['N']}x{w['K']}, full"}
     return {
         "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "single_thread": single,
         "seconds": t, "cpu_model": cpu_model,
         "sample": f"rows 0..{rows - 1} of C ({rows} x {N} outputs, full K={K}) of the same "
                   f"{res['M']}x{N}x{K} GEMM; fp64 triple loop, OpenMP over rows",
@@ -489,7 +590,9 @@ def main():
                     help="target length of the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
-    ap.add_argument("--leg", default="all", choices=["all", "gemm", "gemv", "copy"])
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read and launch-floor ceilings of the GEMV leg")
+    ap.add_argument("--leg", default="all", choices=["all", "gemm", "gemv", "copy", "ceiling"])
     ap.add_argument("--copy-mb", type=int, default=1024)
     args = ap.parse_args()
 
@@ -507,6 +610,10 @@ def main():
 
     if args.leg == "copy":
         copy_leg(args, torch)
+        return
+    if args.leg == "ceiling":
+        _, sets = make_sets("gemv_m1", torch, 2 * MALL_BYTES + 32 * 2 ** 20)
+        print(json.dumps({"leg": "ceiling", **ceiling_leg(args, torch, [b for _, b, _ in sets])}))
         return
     if args.leg == "gemv":
         g = gemv_leg(args, torch, args.gemv_workload)

@@ -307,3 +307,22 @@ def test_attention_plan_variants():
     assert aplan(tm.ATTN_VARIANT_PIPE, d=32)[0] == tm.GEMM_ERR_UNSUPPORTED
     assert aplan(tm.ATTN_VARIANT_AUTO, d=32)[:2] == (0, "attn_simple")
     assert aplan(4)[0] == tm.GEMM_ERR_ARG
+
+
+def test_ceiling_library_exports_and_checks():
+    """libtmm_ceiling.so (the measurement kernels bench.py runs beside the GEMV) exports what
+    include/ceiling.h declares and rejects bad arguments on the host."""
+    import re
+    from tiled_matmul_amd import ceiling as cl
+    lib = cl.library()
+    text = re.sub(r"/\*.*?\*/", "", open(cl.HEADER).read(), flags=re.S)
+    names = re.findall(r"^\s*int\s+(ceiling_\w+)\s*\(", text, re.M)
+    assert sorted(names) == ["ceiling_launch_floor", "ceiling_stream_read"]
+    for n in names:
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+    assert lib.ceiling_stream_read(P, 1000, P, 256, 256, None) == 1        # not a multiple of 16
+    assert lib.ceiling_stream_read(P + 8, 1024, P, 256, 256, None) == 1    # misaligned
+    assert lib.ceiling_stream_read(P, 1 << 31, P, 256, 256, None) == 1     # too large
+    assert lib.ceiling_stream_read(P, 1024, P, 256, 96, None) == 1         # block not a multiple of 64
+    assert lib.ceiling_stream_read(None, 1024, P, 256, 256, None) == 1
+    assert lib.ceiling_launch_floor(0, 64, None) == 1

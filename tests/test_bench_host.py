@@ -16,9 +16,35 @@ def test_sclk_sampler_reads_the_current_level(tmp_path):
     with s:
         time.sleep(0.05)
     r = s.summary()
-    assert r["median"] == 1897 and r["min"] == 1897 and r["max"] == 1897 and r["samples"] >= 1
-    assert s.summary(wall_s=0.45)["median"] == 1897
-    assert s.summary(wall_s=0.1) is None          # too short for the amdgpu driver's reading
+    assert r["median"] == 1897 and r["min"] == 1897 and r["max"] == 1897 and r["samples"] >= 2
+    assert r["start"] == 1897 and r["end"] == 1897
+    # a timed region of a few milliseconds still reports (its start and end readings)
+    s2 = bench.SclkSampler()
+    s2.path = str(f)
+    with s2:
+        pass
+    r2 = s2.summary(wall_s=0.002)
+    assert r2["median"] == 1897 and r2["samples"] >= 2 and r2["timed_region_s"] == 0.002
+
+
+def test_trace_taken_only_on_the_same_sources_and_launch(tmp_path, monkeypatch):
+    import json
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    sha = bench.kernel_source_sha("ring4_256")
+    d = {"kernel_source_sha": sha, "grid": 256, "block": 256, "avg_us": 100.0, "median_us": 99.0,
+         "dispatches": 20, "command": "x"}
+    json.dump(d, open(tmp_path / "profiles" / "trace_ring4_256_w1.json", "w"))
+    t = bench.trace_for("ring4_256", "w1", 256, 256)
+    r = bench.traced_rate(t, 2.0e14 * 1e-4, 2500.0, 1e12)       # 2e14 FLOP/s over 100 us
+    assert abs(r["achieved_avg"] - 200.0) < 1e-9 and abs(r["frac_avg"] - 0.08) < 1e-12
+    assert abs(r["achieved_median"] - 200.0 * 100 / 99) < 1e-9
+    assert bench.trace_for("ring4_256", "w1", 240, 256) is None          # another launch
+    assert bench.trace_for("ring4_256", "w2", 256, 256) is None          # no summary
+    d["kernel_source_sha"] = "0" * 16
+    json.dump(d, open(tmp_path / "profiles" / "trace_ring4_256_w3.json", "w"))
+    assert bench.trace_for("ring4_256", "w3", 256, 256) is None          # other sources
+    assert bench.traced_rate(None, 1.0, 1.0, 1.0) is None
 
 
 def test_sclk_sampler_without_sysfs():

@@ -340,16 +340,27 @@ def test_dtv_workload_sampled_rows(name):
             assert np.isfinite(got).all()
 
 
+@pytest.mark.parametrize("integer", [False, True])
 @pytest.mark.parametrize("out_dtype", [OUT_FP32, OUT_BF16])
-def test_workload_batched(out_dtype):
+def test_workload_batched(out_dtype, integer):
+    """All 64 items of the batched workload at its full shape through
+    gemm_bf16_strided_batched (the launch the bench times), C filled with NaN first: every item
+    against the oracle within the bound on the workload's values, and bitwise on integers."""
     name = "batched_64x256x256x1024"
     w = synth.WORKLOADS[name]
     batch, M, N, K = w["batch"], w["M"], w["N"], w["K"]
-    pairs = [synth.make_operands(name, item=b) for b in range(batch)]
+    if integer:
+        sa, sb = synth.seeds(w["cfg"])
+        pairs = [(synth.integers(M, K, sa + 2 * b), synth.integers(N, K, sb + 2 * b)) for b in range(batch)]
+    else:
+        pairs = [synth.make_operands(name, item=b) for b in range(batch)]
     A = to_device(np.stack([p[0] for p in pairs]))
     B = to_device(np.stack([p[1] for p in pairs]))
-    C = empty_out(M, N, out_dtype, batch=batch)
+    C = empty_out(M, N, out_dtype, batch=batch, fill=float("nan") if out_dtype == OUT_FP32 else -1)
     tm.gemm_bf16_strided_batched(batch, M, N, K, A, K, M * K, B, K, N * K, C, N, M * N, out_dtype)
     h = out_to_host(C, M, N, N, out_dtype, batch=batch)
-    for b in (0, 1, 17, 38, 63):
-        assert_bound(h[b], pairs[b][0], pairs[b][1], K, out_dtype, what=f"item {b}")
+    for b in range(batch):
+        if integer:
+            assert_exact(h[b], pairs[b][0], pairs[b][1], K, out_dtype, what=f"item {b}")
+        else:
+            assert_bound(h[b], pairs[b][0], pairs[b][1], K, out_dtype, what=f"item {b}")

@@ -58,5 +58,20 @@ def build_library(jobs: int | None = None, out: str = LIB, defines=(), csrc: str
     return out
 
 
+CEILING_SRC = os.path.join(PKG, "ceiling", "ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "ceiling", "libtmm_ceiling.so")
+
+
+def build_ceiling() -> str:
+    """Compile libtmm_ceiling.so (the measurement kernels bench.py runs beside the GEMV)."""
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [HIPCC, *CFLAGS, "-shared", CEILING_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CEILING_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
+
+
 if __name__ == "__main__":
     print(build_library())

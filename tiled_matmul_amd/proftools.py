@@ -11,6 +11,11 @@
         of a plain copy kernel to what the same counter read for it; stamped with the source
         hash of planner kernel ID (ring4_256, gemv_lds, ...) and, with --grid G --block B, the
         launch shape it was measured on.
+    python -m tiled_matmul_amd.proftools trace <kernel_trace.csv> --kernel SUBSTR --plan-kernel ID \
+        --workload NAME --skip-first N --grid G --block B --command "..." --out profiles/trace_<ID>_<NAME>.json
+        duration statistics of the kernel whose name contains SUBSTR (without its first N
+        dispatches), stamped like a traffic summary, for bench.py to report beside its own
+        HIP-event timing
     python -m tiled_matmul_amd.proftools sha ID
         that source hash: the shared device headers and the file that defines kernel ID
     python -m tiled_matmul_amd.proftools mfma <run_counter_collection.csv> <run_kernel_trace.csv> \
@@ -138,6 +143,24 @@ def mfma_summary(counters, trace, substr, peak_tflops=2500.0):
     return res
 
 
+def trace_summary(trace, substr, plan_kernel, workload, skip_first, grid, block, command, out=None):
+    """Durations of the dispatches of the kernel whose name contains substr (all matching
+    names pooled, in launch order, the first skip_first dropped), as a summary bench.py reads."""
+    v = [x for name, d in kernel_durations(trace).items() if substr in name for x in d]
+    if len(v) <= skip_first:
+        raise SystemExit(f"{len(v)} dispatches of a kernel containing {substr!r}, skip {skip_first}")
+    v = v[skip_first:]
+    q = duration_quantiles(v)
+    res = {"kernel": substr, "plan_kernel": plan_kernel, "workload": workload,
+           "kernel_source_sha": kernel_source_sha(plan_kernel), "grid": grid, "block": block,
+           "command": command, "skip_first": skip_first, "dispatches": len(v),
+           **{f"{k}_us": val for k, val in q.items()}}
+    if out:
+        with open(out, "w") as f:
+            json.dump(res, f, indent=1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -150,6 +173,13 @@ def main():
         t.add_argument(a, required=True)
     t.add_argument("--grid", type=int)
     t.add_argument("--block", type=int)
+    tr = sub.add_parser("trace")
+    tr.add_argument("trace")
+    for a_ in ("--kernel", "--plan-kernel", "--workload", "--command", "--out"):
+        tr.add_argument(a_, required=True)
+    tr.add_argument("--skip-first", type=int, default=0)
+    tr.add_argument("--grid", type=int)
+    tr.add_argument("--block", type=int)
     h = sub.add_parser("sha")
     h.add_argument("kernel")
     m = sub.add_parser("mfma")
@@ -165,6 +195,10 @@ def main():
         return
     if a.cmd == "mfma":
         print(json.dumps(mfma_summary(a.counters, a.trace, a.kernel, a.peak_tflops)))
+        return
+    if a.cmd == "trace":
+        print(json.dumps(trace_summary(a.trace, a.kernel, a.plan_kernel, a.workload, a.skip_first,
+                                       a.grid, a.block, a.command, a.out), indent=1))
         return
     if a.cmd == "stats":
         print("| Kernel | Calls | Avg (us) | Median (us) | Min (us) | p90 (us) | Max (us) |")
