@@ -48,6 +48,7 @@ extern "C" {
 #define GEMM_ERR_ARCH 4        /* current device is not gfx950, or no device               */
 #define GEMM_ERR_LAUNCH 5      /* the HIP runtime rejected the kernel launch              */
 #define GEMM_ERR_UNSUPPORTED 6 /* the requested variant cannot run these arguments         */
+#define GEMM_ERR_SCRATCH 7     /* the call needs more than the library's static scratch    */
 
 /* Output element types. */
 #define GEMM_OUT_FP32 0        /* C is float                                              */
@@ -240,6 +241,29 @@ int gemm_bf16_splitk_plan(int a_layout, int b_layout, int splits, int64_t batch,
                           const void* C, int64_t ldc, int64_t strideC,
                           int out_dtype, const void* workspace, int64_t workspace_bytes,
                           int num_cus, int* splits_out, int* kernel_id, int64_t* grid_x);
+
+/*
+ * gemm_bf16_splitk without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the fp32 partials go to a scratch array the library holds in device memory,
+ * GEMM_SCRATCH_BYTES per device, reserved when the library is loaded and kept until the
+ * process ends.  Nothing is allocated or freed in the call.
+ *   splits   as gemm_bf16_splitk; with 0 the automatic count is limited to what the scratch
+ *            holds.  An explicit count whose partials (S * batch * M * N * 4 bytes, S capped
+ *            at ceil(K / 64)) exceed GEMM_SCRATCH_BYTES returns GEMM_ERR_SCRATCH and launches
+ *            nothing.
+ * Other arguments, results and errors as gemm_bf16_splitk; the result is bitwise that of
+ * gemm_bf16_splitk with the same S.  Every call on one device uses that device's one scratch
+ * array, and each call writes every partial it reads (nothing needs to start at zero), but
+ * calls that overlap in time on one device race: order them on one stream.
+ */
+#define GEMM_SCRATCH_BYTES (64ll << 20)
+int gemm_bf16_splitk_noalloc(int a_layout, int b_layout, int splits, int64_t batch,
+                             int64_t M, int64_t N, int64_t K,
+                             const void* A, int64_t lda, int64_t strideA,
+                             const void* B, int64_t ldb, int64_t strideB,
+                             void* C, int64_t ldc, int64_t strideC,
+                             int out_dtype, void* stream);
 
 /* Name of a kernel id from gemm_bf16_plan ("?" if unknown).  Static storage. */
 const char* gemm_bf16_kernel_name(int kernel_id);

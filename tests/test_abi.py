@@ -20,8 +20,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tm.gemm_bf16_version() == 7
-    for s in range(7):
+    assert tm.gemm_bf16_version() == 8
+    for s in range(8):
         assert tm.gemm_bf16_status_string(s).startswith("GEMM_")
     assert tm.gemm_bf16_status_string(99) == "unknown status"
     assert tm.gemm_bf16_kernel_name(4) == "pipe_256"
@@ -307,6 +307,22 @@ def test_attention_plan_variants():
     assert aplan(tm.ATTN_VARIANT_PIPE, d=32)[0] == tm.GEMM_ERR_UNSUPPORTED
     assert aplan(tm.ATTN_VARIANT_AUTO, d=32)[:2] == (0, "attn_simple")
     assert aplan(4)[0] == tm.GEMM_ERR_ARG
+
+
+def test_splitk_noalloc_host_checks():
+    """gemm_bf16_splitk_noalloc's argument checks run on the host before any device call."""
+    f = tm.library().gemm_bf16_splitk_noalloc
+    args = lambda splits, M=1024, N=4096, K=4096, batch=1: (0, 0, splits, batch, M, N, K, P, K, 0, P, K, 0, P, N,
+                                                           0, 0, None)
+    assert f(*args(-1)) == tm.GEMM_ERR_ARG
+    # 8 ranges of 1024 x 4096 fp32 partials: 128 MiB, beyond the 64 MiB scratch
+    assert f(*args(8)) == tm.GEMM_ERR_SCRATCH
+    # the count is capped at ceil(K / 64) before the check: K = 320 gives at most 5 ranges of
+    # 16 MiB, 80 MiB (the accepted side of the limit launches work, so no fake pointer takes it)
+    assert f(*args(80, K=320)) == tm.GEMM_ERR_SCRATCH
+    assert tm.gemm_bf16_status_string(tm.GEMM_ERR_SCRATCH).startswith("GEMM_ERR_SCRATCH")
+    # a bad argument is reported before the size
+    assert f(*(args(8)[:8] + (100,) + args(8)[9:])) == tm.GEMM_ERR_ARG
 
 
 def test_ceiling_library_exports_and_checks():

@@ -30,6 +30,8 @@ GEMM_ERR_DTYPE = 3
 GEMM_ERR_ARCH = 4
 GEMM_ERR_LAUNCH = 5
 GEMM_ERR_UNSUPPORTED = 6
+GEMM_ERR_SCRATCH = 7
+GEMM_SCRATCH_BYTES = 64 << 20
 
 GEMM_OUT_FP32 = 0
 GEMM_OUT_BF16 = 1
@@ -104,6 +106,7 @@ def _load():
     lib.gemm_bf16_layout_plan.argtypes = [_int, _int, _int] + batched + [
         _int, ctypes.POINTER(_int), ctypes.POINTER(_i64), ctypes.POINTER(_int)]
     lib.gemm_bf16_splitk.argtypes = [_int, _int, _int] + batched + [_vp, _i64, _vp]
+    lib.gemm_bf16_splitk_noalloc.argtypes = [_int, _int, _int] + batched + [_vp]
     lib.gemm_bf16_splitk_plan.argtypes = [_int, _int, _int] + batched + [
         _vp, _i64, _int, ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_i64)]
     mx = [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int]
@@ -125,6 +128,7 @@ def _load():
     for f in ("gemm_bf16", "gemm_bf16_strided_batched", "gemm_bf16_variant",
               "gemm_bf16_validate", "gemm_bf16_plan", "gemm_bf16_version", "gemm_bf16_layout",
               "gemm_bf16_layout_validate", "gemm_bf16_layout_plan", "gemm_bf16_splitk",
+              "gemm_bf16_splitk_noalloc",
               "gemm_bf16_splitk_plan"):
         getattr(lib, f).restype = _int
     lib.gemm_bf16_kernel_name.argtypes = [_int]
@@ -244,6 +248,13 @@ def gemm_bf16_splitk(a_layout, b_layout, splits, batch, M, N, K, A, lda, strideA
                                     strideA, _ptr(B), ldb, strideB, _ptr(C), ldc, strideC,
                                     out_dtype, _ptr(workspace), workspace_bytes,
                                     _stream(stream)), "gemm_bf16_splitk")
+
+
+def gemm_bf16_splitk_noalloc(a_layout, b_layout, splits, batch, M, N, K, A, lda, strideA, B, ldb,
+                             strideB, C, ldc, strideC, out_dtype, stream=None):
+    _check(_load().gemm_bf16_splitk_noalloc(a_layout, b_layout, splits, batch, M, N, K, _ptr(A), lda,
+                                            strideA, _ptr(B), ldb, strideB, _ptr(C), ldc, strideC,
+                                            out_dtype, _stream(stream)), "gemm_bf16_splitk_noalloc")
 
 
 def gemm_bf16_splitk_plan(a_layout, b_layout, splits, batch, M, N, K, A, lda, strideA, B, ldb,

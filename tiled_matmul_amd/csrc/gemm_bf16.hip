@@ -14,7 +14,7 @@ using namespace tmm;
 
 namespace {
 
-constexpr int kVersion = 7;
+constexpr int kVersion = 8;
 constexpr int kDefaultCUs = 256;        // MI355X
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t k2G = int64_t(1) << 31;
@@ -395,6 +395,46 @@ int run_splitk(const Shape& s, int splits, void* ws, int64_t ws_bytes, void* str
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// --- split K without a workspace argument ----------------------------------------------
+// The fp32 partials of gemm_bf16_splitk_noalloc live here: GEMM_SCRATCH_BYTES per device, in
+// the code object's device memory.  Host code never passes `scratch` itself to a kernel (in
+// host code the name is a stand-in, not a device address): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and kept.
+__device__ __align__(256) float scratch[GEMM_SCRATCH_BYTES / 4];
+
+std::mutex g_scratch_mu;
+void* g_scratch[64];
+
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch[dev] = ptr;
+    }
+    return g_scratch[dev];
+}
+
+int run_splitk_noalloc(const Shape& s, int splits, void* stream) {
+    int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
+                      s.out);
+    if (rc != GEMM_OK) return rc;
+    if (splits < 0) return GEMM_ERR_ARG;
+    if (s.batch == 0 || s.M == 0 || s.N == 0) return GEMM_OK;
+    if (splits > 0 && s.K > 0) {   // an explicit count must fit (S capped at the K blocks)
+        const __int128 S = std::min<int64_t>(splits, cdiv(s.K, 64));
+        if (S > 1 && S * s.batch * s.M * s.N * 4 > GEMM_SCRATCH_BYTES) return GEMM_ERR_SCRATCH;
+    }
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != GEMM_OK) return rc;
+    void* ws = scratch_on_current_device();
+    if (ws == nullptr) return GEMM_ERR_LAUNCH;
+    return run_splitk(s, splits, ws, GEMM_SCRATCH_BYTES, stream);
+}
+
 Shape shape(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t sA,
             const void* B, int64_t ldb, int64_t sB, const void* C, int64_t ldc, int64_t sC, int out,
             int la = GEMM_LAYOUT_K_MAJOR, int lb = GEMM_LAYOUT_K_MAJOR) {
@@ -673,6 +713,14 @@ int gemm_bf16_splitk(int a_layout, int b_layout, int splits, int64_t batch, int6
         splits, workspace, workspace_bytes, stream);
 }
 
+int gemm_bf16_splitk_noalloc(int a_layout, int b_layout, int splits, int64_t batch, int64_t M, int64_t N,
+                             int64_t K, const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb,
+                             int64_t strideB, void* C, int64_t ldc, int64_t strideC, int out_dtype, void* stream) {
+    return run_splitk_noalloc(
+        shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype, a_layout, b_layout),
+        splits, stream);
+}
+
 int gemm_bf16_splitk_plan(int a_layout, int b_layout, int splits, int64_t batch, int64_t M, int64_t N,
                           int64_t K, const void* A, int64_t lda, int64_t strideA, const void* B, int64_t ldb,
                           int64_t strideB, const void* C, int64_t ldc, int64_t strideC, int out_dtype,
@@ -803,6 +851,7 @@ const char* gemm_bf16_status_string(int status) {
         case GEMM_ERR_ARCH: return "GEMM_ERR_ARCH: current device is not a gfx950 (MI355X)";
         case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: the HIP runtime rejected the launch";
         case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: variant cannot run these arguments";
+        case GEMM_ERR_SCRATCH: return "GEMM_ERR_SCRATCH: the partials exceed the library's 64 MiB scratch";
         default: return "unknown status";
     }
 }
