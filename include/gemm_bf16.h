@@ -67,6 +67,7 @@ extern "C" {
 #define GEMM_VARIANT_RING8 8       /* steps 4-6, separate A and B rings, loads spread, 8 waves */
 #define GEMM_VARIANT_RING4 9       /* the same with 4 waves of 128x128 register tiles          */
 #define GEMM_VARIANT_DTV 10        /* ring4's tile with A loaded into MFMA registers, B in LDS */
+#define GEMM_VARIANT_ROLES 11      /* step 7 with fixed roles: 4 load-only, 4 MFMA-only waves  */
 
 /* Operand layouts (gemm_bf16_layout).  The page "读书笔记-《面向机器学习系统的现代 GPU
  * 编程》", section "三个核心概念：scope、layout、dispatch", names the two ways a GEMM

@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tm.gemm_bf16_version() == 8
+    assert tm.gemm_bf16_version() == 9
     for s in range(8):
         assert tm.gemm_bf16_status_string(s).startswith("GEMM_")
     assert tm.gemm_bf16_status_string(99) == "unknown status"
@@ -125,7 +125,14 @@ def test_plan_variant_preconditions():
     assert plan(variant=10)[3] == 256
     assert plan(variant=10, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED      # 16-byte chunks need K % 8 == 0
     assert plan(variant=10, A=P + 8)[0] == tm.GEMM_ERR_UNSUPPORTED     # and 16-byte aligned rows
-    assert plan(variant=11)[0] == tm.GEMM_ERR_ARG
+    # fixed producer / consumer waves: 256 x 128 tiles, 8 waves, K % 8 == 0, 4-byte aligned rows
+    assert plan(variant=11) == (0, "roles_256x128", 256, 512)
+    assert plan(variant=11, M=4096, N=2048)[:3] == (0, "roles_256x128", 256)
+    assert plan(variant=11, M=512, N=512)[:3] == (0, "roles_256x128", 8)
+    assert plan(variant=11, K=4100)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=11, A=P + 2)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert plan(variant=11, A=P + 4)[:2] == (0, "roles_256x128")
+    assert plan(variant=12)[0] == tm.GEMM_ERR_ARG
     assert plan(variant=1)[1] == "simple_64"
     assert plan(variant=2)[1] == "mfma_128"
 
@@ -186,9 +193,9 @@ def test_layout_plan():
     assert lplan(KM, MN, variant=1)[:2] == (0, "simple_64")
     assert lplan(KM, MN, variant=9)[:2] == (0, "ring4_256")
     assert lplan(KM, MN, variant=9, N=4093)[0] == tm.GEMM_ERR_UNSUPPORTED
-    for variant in (2, 3, 4, 5, 6, 7, 8, 10):
+    for variant in (2, 3, 4, 5, 6, 7, 8, 10, 11):
         assert lplan(KM, MN, variant=variant)[0] == tm.GEMM_ERR_UNSUPPORTED, variant
-    assert lplan(KM, MN, variant=11)[0] == tm.GEMM_ERR_ARG
+    assert lplan(KM, MN, variant=12)[0] == tm.GEMM_ERR_ARG
     # K = 0: zero fill in any layout
     assert lplan(MN, MN, K=0, lda=4096, ldb=4096)[:2] == (0, "zero_fill")
     # both K-major: the K-major planner (the GEMV path included)

@@ -25,7 +25,8 @@ pytestmark = pytest.mark.gpu
 V = tm
 ALL_TILED = [V.GEMM_VARIANT_SIMPLE, V.GEMM_VARIANT_MFMA, V.GEMM_VARIANT_PIPELINED,
              V.GEMM_VARIANT_PERSISTENT, V.GEMM_VARIANT_SPECIALIZED, V.GEMM_VARIANT_PINGPONG,
-             V.GEMM_VARIANT_RING8, V.GEMM_VARIANT_RING4, V.GEMM_VARIANT_DTV, V.GEMM_VARIANT_AUTO]
+             V.GEMM_VARIANT_RING8, V.GEMM_VARIANT_RING4, V.GEMM_VARIANT_DTV, V.GEMM_VARIANT_ROLES,
+             V.GEMM_VARIANT_AUTO]
 
 
 @pytest.fixture(scope="module", autouse=True)

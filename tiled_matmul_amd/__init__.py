@@ -63,13 +63,14 @@ GEMM_VARIANT_PINGPONG = 7
 GEMM_VARIANT_RING8 = 8
 GEMM_VARIANT_RING4 = 9
 GEMM_VARIANT_DTV = 10
+GEMM_VARIANT_ROLES = 11
 
 VARIANTS = {
     "auto": GEMM_VARIANT_AUTO, "simple": GEMM_VARIANT_SIMPLE, "mfma": GEMM_VARIANT_MFMA,
     "pipelined": GEMM_VARIANT_PIPELINED, "persistent": GEMM_VARIANT_PERSISTENT,
     "specialized": GEMM_VARIANT_SPECIALIZED, "gemv": GEMM_VARIANT_GEMV,
     "pingpong": GEMM_VARIANT_PINGPONG, "ring8": GEMM_VARIANT_RING8, "ring4": GEMM_VARIANT_RING4,
-    "dtv": GEMM_VARIANT_DTV,
+    "dtv": GEMM_VARIANT_DTV, "roles": GEMM_VARIANT_ROLES,
 }
 
 

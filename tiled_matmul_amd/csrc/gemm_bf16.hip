@@ -14,7 +14,7 @@ using namespace tmm;
 
 namespace {
 
-constexpr int kVersion = 8;
+constexpr int kVersion = 9;
 constexpr int kDefaultCUs = 256;        // MI355X
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t k2G = int64_t(1) << 31;
@@ -191,6 +191,20 @@ int plan_dtv(const Shape& s, int cus, Plan& p) {
     return GEMM_OK;
 }
 
+// Fixed producer and consumer waves: K-major operands with the pipelined kernels' loads, K a
+// multiple of 8, 256 x 128 tiles, persistent.
+int plan_roles(const Shape& s, int cus, Plan& p) {
+    if (s.la != GEMM_LAYOUT_K_MAJOR || s.lb != GEMM_LAYOUT_K_MAJOR || s.K % 8 || !pipe_loads_ok(s, 256))
+        return GEMM_ERR_UNSUPPORTED;
+    tile_grid(s, 256, 128, p);
+    p.kernel = K_ROLES;
+    p.grid_x = std::min(p.grid.total, cus);
+    p.grid_y = p.grid_z = 1;
+    p.block = 512;
+    p.vec_store = vec_store_ok(s);
+    return GEMM_OK;
+}
+
 bool gemv_ok(const Shape& s) {
     if (s.M > 16 || s.batch != 1) return false;
     if (!aligned(s.A, 16) || !aligned(s.B, 16) || s.lda % 8 || s.ldb % 8 || s.K % 8) return false;
@@ -247,7 +261,7 @@ int plan_layout(int variant, const Shape& s, int cus, Plan& p) {
 }
 
 int make_plan(int variant, const Shape& s, int cus, Plan& p) {
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_DTV) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_ROLES) return GEMM_ERR_ARG;
     p = Plan{};
     if (s.batch == 0 || s.M == 0 || s.N == 0) {
         p.kernel = K_NONE;
@@ -272,6 +286,7 @@ int make_plan(int variant, const Shape& s, int cus, Plan& p) {
         case GEMM_VARIANT_RING8: return plan_spec(s, cus, p, K_RING8_256);
         case GEMM_VARIANT_RING4: return plan_spec(s, cus, p, K_RING4_256);
         case GEMM_VARIANT_DTV: return plan_dtv(s, cus, p);
+        case GEMM_VARIANT_ROLES: return plan_roles(s, cus, p);
         default: break;
     }
     // AUTO
@@ -287,7 +302,7 @@ int run(int variant, const Shape& s, void* stream) {
     int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
                       s.out);
     if (rc != GEMM_OK) return rc;
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_DTV) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_ROLES) return GEMM_ERR_ARG;
     if (s.batch == 0 || s.M == 0 || s.N == 0) return GEMM_OK;
     int cus = 0;
     rc = current_device(&cus);
@@ -315,6 +330,7 @@ int run(int variant, const Shape& s, void* stream) {
         case K_RING8_256:
         case K_RING4_256: e = launch_ring(g, s.out, p, st); break;
         case K_DTV_256: e = launch_dtv(g, s.out, p, st); break;
+        case K_ROLES: e = launch_roles(g, s.out, p, st); break;
         case K_GEMV: e = launch_gemv(g, s.out, p, st); break;
         case K_GEMV_LDS: e = launch_gemv_lds(g, s.out, p, st); break;
         default: return GEMM_ERR_UNSUPPORTED;
@@ -445,7 +461,7 @@ int plan_into(int variant, const Shape& s, int num_cus, int* kernel_id, int64_t*
     int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
                       s.out);
     if (rc != GEMM_OK) return rc;
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_DTV) return GEMM_ERR_ARG;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_ROLES) return GEMM_ERR_ARG;
     Plan p;
     rc = make_plan(variant, s, num_cus > 0 ? num_cus : kDefaultCUs, p);
     if (rc != GEMM_OK) return rc;
@@ -831,6 +847,7 @@ const char* gemm_bf16_kernel_name(int k) {
         case K_RING8_256: return "ring8_256";
         case K_RING4_256: return "ring4_256";
         case K_DTV_256: return "dtv_256";
+        case K_ROLES: return "roles_256x128";
         case K_MX_RING_256: return "mx_ring_256";
         case K_MX_SIMPLE_64: return "mx_simple_64";
         case K_ATTN_SIMPLE: return "attn_simple";

@@ -30,7 +30,8 @@ enum KernelId {
     K_ATTN_MFMA = 17,       //   MFMA tiles of queries x keys, online softmax (d = 64, 128)
     K_DTV_256 = 18,         // steps 4-6 with the A operand loaded straight into MFMA registers, B ring in LDS
     K_ATTN_PIPE = 19,       //   same, the next block's score MFMAs interleaved with this block's softmax
-    K_COUNT = 20
+    K_ROLES = 20,           // step 7 with fixed roles: 4 load-only + 4 MFMA-only waves, 256 x 128 tile
+    K_COUNT = 21
 };
 
 // Launch shape chosen for a problem (filled by the planner, consumed by the launchers).
@@ -49,6 +50,7 @@ hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s)
 hipError_t launch_pingpong(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_ring(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_dtv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_roles(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs& g, int out, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_mx(const MxArgs& g, int out, const Plan& p, hipStream_t s);

@@ -49,7 +49,7 @@ KERNEL_SOURCE = {
     "pipe_256": "gemm_pipe.hip", "pipe_128": "gemm_pipe.hip", "persist_256": "gemm_pipe.hip",
     "persist_128": "gemm_pipe.hip", "spec_256": "gemm_pipe.hip", "pingpong_256": "gemm_pingpong.hip",
     "ring8_256": "gemm_ring.hip", "ring4_256": "gemm_ring.hip", "splitk_reduce": "gemm_ring.hip",
-    "dtv_256": "gemm_dtv.hip", "gemv": "gemv.hip", "gemv_lds": "gemv.hip",
+    "dtv_256": "gemm_dtv.hip", "roles_256x128": "gemm_roles.hip", "gemv": "gemv.hip", "gemv_lds": "gemv.hip",
     "mx_ring_256": "gemm_mx.hip", "mx_simple_64": "gemm_mx.hip",
     "attn_simple": "attention.hip", "attn_mfma": "attention.hip", "attn_pipe": "attention.hip",
 }
