@@ -61,13 +61,14 @@ def to_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def make_sets(name, torch, min_bytes, la=0, lb=0):
+def make_sets(name, torch, min_bytes, la=0, lb=0, pitch=None):
     """Enough copies of the workload's operands (and outputs) to exceed min_bytes.  Device
     operands are (M, K) and (N, K), or (batch, M, K) and (batch, N, K) for a batched
-    workload; the host arrays returned are batch item 0's."""
+    workload (rows `pitch` elements apart if given, the padding NaN); the host arrays returned
+    are batch item 0's."""
     w = synth.WORKLOADS[name]
     M, N, K, out, batch = w["M"], w["N"], w["K"], w["out"], w["batch"]
-    items = [synth.make_operands(name, item=b) for b in range(batch)]
+    items = [synth.make_operands(name, item=b, lda=pitch, ldb=pitch) for b in range(batch)]
     A, B = items[0]
     if batch == 1:
         Ad, Bd = to_dev(A, torch), to_dev(B, torch)
@@ -231,12 +232,28 @@ def gemm_leg(args, torch):
     lb = tm.GEMM_LAYOUT_MN_MAJOR if args.b_layout == "mn" else tm.GEMM_LAYOUT_K_MAJOR
     lda = M if la == tm.GEMM_LAYOUT_MN_MAJOR else K
     ldb = N if lb == tm.GEMM_LAYOUT_MN_MAJOR else K
+    pitch = None
+    if args.pad_pitch:
+        if la != tm.GEMM_LAYOUT_K_MAJOR or lb != tm.GEMM_LAYOUT_K_MAJOR:
+            raise SystemExit("--pad-pitch takes K-major operands")
+        pitch = lda = ldb = -(-K // 64) * 64
+        if batch > 1:
+            sA, sB = M * pitch, N * pitch
     log(f"[bench] generating {name} operands")
-    (A, B), sets = make_sets(name, torch, args.rotate_mb * 2 ** 20, la, lb)
+    (A, B), sets = make_sets(name, torch, args.rotate_mb * 2 ** 20, la, lb, pitch)
     variant = tm.VARIANTS[args.variant]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     splits = None
-    if args.splits is not None:
+    sk_ws = None
+    if args.streamk is not None:
+        # stream-K with atomic work claiming: a zeroed workspace of the size the plan gives
+        rc, ws_bytes, dp, sk, slots, grid = tm.gemm_bf16_streamk_plan(
+            args.streamk, batch, M, N, K, sets[0][0], lda, sA, sets[0][1], ldb, sB, sets[0][2], N, sC, out, cus)
+        block = 256
+        kname = "ring4_256"
+        sk_ws = torch.zeros(max(ws_bytes // 4, 64), dtype=torch.int32, device="cuda")
+        splits = {"streamk_mode": args.streamk, "whole_tiles": dp, "cut_tiles": sk, "slots": slots}
+    elif args.splits is not None:
         # split K: plan with an unbounded workspace, then allocate what the plan needs
         rc, splits, kname, grid = tm.gemm_bf16_splitk_plan(
             la, lb, args.splits, batch, M, N, K, sets[0][0], lda, sA, sets[0][1], ldb, sB,
@@ -255,7 +272,10 @@ def gemm_leg(args, torch):
 
     def launch(i):
         a, b, c = sets[i]
-        if splits is not None:
+        if sk_ws is not None:
+            tm.gemm_bf16_streamk(args.streamk, batch, M, N, K, a, lda, sA, b, ldb, sB, c, N, sC, out, sk_ws,
+                                 sk_ws.numel() * 4)
+        elif splits is not None:
             tm.gemm_bf16_splitk(la, lb, args.splits, batch, M, N, K, a, lda, sA, b, ldb, sB, c, N,
                                 sC, out, ws, ws_bytes)
         else:
@@ -272,7 +292,8 @@ def gemm_leg(args, torch):
     nbytes = batch * rl.algorithmic_bytes(M, N, K, obytes)
     return {
         "name": name, "batch": batch, "M": M, "N": N, "K": K,
-        "layouts": f"A {args.a_layout}-major, B {args.b_layout}-major",
+        "layouts": f"A {args.a_layout}-major, B {args.b_layout}-major"
+                   + (f", row pitch {pitch} elements (128-byte aligned rows)" if pitch else ""),
         "out": "fp32" if out == 0 else "bf16",
         "kernel": kname, "grid": grid, "block": block, "ms": ms, "wall_s": wall,
         "splits": splits, "sclk": sclk, "per_chunk": per_chunk,
@@ -502,14 +523,14 @@ def cpu_baseline_leg(res, args, torch):
     A, B, K, N = res["A"], res["B"], res["K"], res["N"]
     threads = oracle.default_threads()
     t0 = time.perf_counter()
-    oracle.gemm(A, B, rows=list(range(threads)), nthreads=threads)   # one row per thread
+    oracle.gemm(A, B, K=K, rows=list(range(threads)), nthreads=threads)   # one row per thread
     t_probe = max(time.perf_counter() - t0, 1e-3)
     rows = int(min(res["M"], max(threads, args.cpu_seconds / t_probe * threads)))
     rows = max(threads, (rows // threads) * threads)
     sel = list(range(rows))
     log(f"[bench] cpu_baseline: oracle on {rows} rows x {N} x {K} with {threads} threads")
     t0 = time.perf_counter()
-    C_ref, Mag = oracle.gemm(A, B, rows=sel, nthreads=threads)
+    C_ref, Mag = oracle.gemm(A, B, K=K, rows=sel, nthreads=threads)
     t = time.perf_counter() - t0
     flops = 2.0 * rows * N * K
     # time_steps launches set i % nsets for timed step i, so the last timed launch used this set
@@ -580,6 +601,12 @@ def main():
     ap.add_argument("--splits", type=int, default=None,
                     help="run the GEMM through gemm_bf16_splitk with this many K ranges "
                          "(0: the library's choice)")
+    ap.add_argument("--streamk", type=int, default=None, choices=[0, 1, 2],
+                    help="run the GEMM through gemm_bf16_streamk with this mode (0 auto, 1 whole "
+                         "tiles only, 2 every tile cut when there are fewer tiles than CUs)")
+    ap.add_argument("--pad-pitch", action="store_true",
+                    help="store A and B rows with a pitch rounded up to 64 elements (128-byte "
+                         "aligned rows) instead of K")
     ap.add_argument("--rotate-mb", type=int, default=512,
                     help="total size of the rotating input/output sets")
     ap.add_argument("--gemv-workload", default="gemv_m1", choices=["gemv_m1", "gemv_m16"],

@@ -11,9 +11,9 @@
  *
  * i.e. C = A * B^T with A (M x K) and B (N x K) row-major bf16, each product exact and the
  * sum accumulated in fp32; C (M x N, row-major) is OVERWRITTEN (no alpha/beta).  The order
- * of the fp32 additions is not specified, but it is fixed: no kernel splits K across
- * workgroups or uses atomics, so repeated calls with the same arguments give bitwise
- * identical results.
+ * of the fp32 additions is not specified, but it is fixed, so repeated calls with the same
+ * arguments give bitwise identical results (gemm_bf16_splitk and gemm_bf16_streamk, which cut
+ * K across workgroups, add the pieces in a fixed order too).
  *
  * Memory and ownership.  A, B and C are device pointers (e.g. from hipMalloc or a torch
  * tensor's data_ptr() on ROCm) owned by the caller; the library keeps no pointer after a call
@@ -242,6 +242,53 @@ int gemm_bf16_splitk_plan(int a_layout, int b_layout, int splits, int64_t batch,
                           const void* C, int64_t ldc, int64_t strideC,
                           int out_dtype, const void* workspace, int64_t workspace_bytes,
                           int num_cus, int* splits_out, int* kernel_id, int64_t* grid_x);
+
+/*
+ * Stream-K with atomic work claiming.  The page "读书笔记-《面向机器学习系统的现代 GPU 编程》"
+ * hands tiles to persistent workgroups from a scheduler ("9 步优化", step 6) and names atomics
+ * as the means for counters and tile claiming ("同步的本质").  Here the 256 x 256 tiles of the
+ * 4-wave ring kernel are the work of one persistent workgroup per compute unit, handed out by an
+ * atomic counter in the workspace: whole tiles first, then, for the last tiles, stream-K slots
+ * of about I / G (tile, K block) iterations each (I the iterations of those tiles, G the
+ * workgroups), which cut the tiles along K so that the workgroups end together.  A tile cut
+ * into several pieces is summed by whichever piece finishes last, adding the fp32 partials in a
+ * fixed order: the result is deterministic (bitwise the same on every run with the same
+ * arguments and device), and differs from gemm_bf16 only in the order of the fp32 additions of
+ * the cut tiles.
+ *   mode   GEMM_STREAMK_AUTO: when there are more tiles than compute units and they do not
+ *          divide evenly, stream-K for the last, partly filled wave and the full wave before it;
+ *          otherwise whole tiles only.
+ *          GEMM_STREAMK_DP: whole tiles only (claimed atomically).  GEMM_STREAMK_ALL: as AUTO,
+ *          and with fewer tiles than compute units every tile is cut.
+ *   workspace, workspace_bytes  device memory owned by the caller, 256-byte aligned, at least
+ *          the size gemm_bf16_streamk_plan returns: 16 KB of counters, then the partials.  The
+ *          16 KB of counters must be zero before the first call on a workspace (e.g. hipMemset
+ *          once); every call leaves them zero again.  Calls that share a workspace must be
+ *          ordered on one stream.
+ * Other arguments as gemm_bf16_strided_batched; both operands K-major, 4-byte aligned with even
+ * pitches and strides (else GEMM_ERR_UNSUPPORTED).  K == 0 zero-fills C (no workspace used).
+ * A workspace that is too small or misaligned: GEMM_ERR_ARG; NULL: GEMM_ERR_NULL.
+ */
+#define GEMM_STREAMK_AUTO 0
+#define GEMM_STREAMK_DP 1
+#define GEMM_STREAMK_ALL 2
+int gemm_bf16_streamk(int mode, int64_t batch, int64_t M, int64_t N, int64_t K,
+                      const void* A, int64_t lda, int64_t strideA,
+                      const void* B, int64_t ldb, int64_t strideB,
+                      void* C, int64_t ldc, int64_t strideC,
+                      int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Host-only plan of gemm_bf16_streamk on a device with `num_cus` compute units (0: 256): the
+ * workspace size it needs, the tiles computed whole (*dp_tiles) and cut (*sk_tiles), the
+ * stream-K slots and the workgroups launched.  Output pointers may be NULL.
+ */
+int gemm_bf16_streamk_plan(int mode, int64_t batch, int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, int64_t strideA,
+                           const void* B, int64_t ldb, int64_t strideB,
+                           const void* C, int64_t ldc, int64_t strideC,
+                           int out_dtype, int num_cus, int64_t* workspace_bytes,
+                           int* dp_tiles, int* sk_tiles, int* sk_slots, int64_t* grid_x);
 
 /*
  * gemm_bf16_splitk without a workspace argument, for callers that cannot allocate device

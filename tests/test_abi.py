@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tm.gemm_bf16_version() == 9
+    assert tm.gemm_bf16_version() == 10
     for s in range(8):
         assert tm.gemm_bf16_status_string(s).startswith("GEMM_")
     assert tm.gemm_bf16_status_string(99) == "unknown status"
@@ -349,3 +349,39 @@ def test_ceiling_library_exports_and_checks():
     assert lib.ceiling_stream_read(P, 1024, P, 256, 96, None) == 1         # block not a multiple of 64
     assert lib.ceiling_stream_read(None, 1024, P, 256, 256, None) == 1
     assert lib.ceiling_launch_floor(0, 64, None) == 1
+
+
+def kplan(mode, M=4096, N=4096, K=4096, batch=1, cus=256, A=P, lda=None):
+    lda = K if lda is None else lda
+    sA, sB, sC = (M * lda, N * lda, M * N) if batch > 1 else (0, 0, 0)
+    return tm.gemm_bf16_streamk_plan(mode, batch, M, N, K, A, lda, sA, P, lda, sB, P, N, sC, 0, cus)
+
+
+def test_streamk_plan():
+    AUTO, DP, ALL = tm.GEMM_STREAMK_AUTO, tm.GEMM_STREAMK_DP, tm.GEMM_STREAMK_ALL
+    # 256 tiles on 256 compute units: whole tiles only, the 16 KB of counters only
+    rc, ws, dp, sk, slots, grid = kplan(AUTO)
+    assert (rc, dp, sk, slots, grid) == (0, 256, 0, 0, 256) and ws == 16384
+    # 289 tiles (one wave and 33): all 289 as stream-K slots of ceil(289 * 64 / 256) = 73 blocks
+    rc, ws, dp, sk, slots, grid = kplan(AUTO, M=4352, N=4352)
+    assert (rc, dp, sk) == (0, 0, 289)
+    assert slots == -(-289 * 64 // 73) == 254 and grid == 254
+    assert ws == 16384 + slots * 2 * 256 * 256 * 4
+    # 600 tiles (two waves and 88): 256 whole, then 256 + 88 cut
+    rc, ws, dp, sk, slots, grid = kplan(AUTO, M=6144, N=6400)
+    assert (rc, dp, sk, grid) == (0, 256, 344, 256)
+    # fewer tiles than compute units: whole tiles (AUTO, DP), all cut (ALL)
+    assert kplan(AUTO, M=3000, N=5000, K=4096)[2:5] == (240, 0, 0)
+    rc, ws, dp, sk, slots, grid = kplan(ALL, M=3000, N=5000, K=4096)
+    assert (dp, sk, slots, grid) == (0, 240, 256, 256)
+    assert kplan(DP, M=4352, N=4352)[2:5] == (289, 0, 0)
+    # at least 4 K blocks per slot: 16 tiles x 16 blocks -> 64 slots of 4
+    assert kplan(ALL, M=1000, N=1000, K=1000)[2:6] == (0, 16, 64, 64)
+    # fewer than 4 blocks per tile: slots of 4 blocks spanning two tiles
+    assert kplan(ALL, M=1000, N=1000, K=136)[2:6] == (0, 16, 12, 12)
+    # errors: unknown mode, unaligned rows (ring kernel preconditions)
+    assert kplan(3)[0] == tm.GEMM_ERR_ARG
+    assert kplan(AUTO, A=P + 2)[0] == tm.GEMM_ERR_UNSUPPORTED
+    assert kplan(AUTO, K=4095, lda=4095)[0] == tm.GEMM_ERR_UNSUPPORTED
+    # a device beyond 800 compute units would need more than the 16 KB of counters
+    assert kplan(AUTO, cus=900, M=8192, N=8192)[0] == tm.GEMM_ERR_UNSUPPORTED

@@ -33,6 +33,10 @@ GEMM_ERR_UNSUPPORTED = 6
 GEMM_ERR_SCRATCH = 7
 GEMM_SCRATCH_BYTES = 64 << 20
 
+GEMM_STREAMK_AUTO = 0
+GEMM_STREAMK_DP = 1
+GEMM_STREAMK_ALL = 2
+
 GEMM_OUT_FP32 = 0
 GEMM_OUT_BF16 = 1
 
@@ -108,6 +112,10 @@ def _load():
         _int, ctypes.POINTER(_int), ctypes.POINTER(_i64), ctypes.POINTER(_int)]
     lib.gemm_bf16_splitk.argtypes = [_int, _int, _int] + batched + [_vp, _i64, _vp]
     lib.gemm_bf16_splitk_noalloc.argtypes = [_int, _int, _int] + batched + [_vp]
+    lib.gemm_bf16_streamk.argtypes = [_int] + batched + [_vp, _i64, _vp]
+    lib.gemm_bf16_streamk_plan.argtypes = [_int] + batched + [
+        _int, ctypes.POINTER(_i64), ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_int),
+        ctypes.POINTER(_i64)]
     lib.gemm_bf16_splitk_plan.argtypes = [_int, _int, _int] + batched + [
         _vp, _i64, _int, ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_i64)]
     mx = [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int]
@@ -129,7 +137,7 @@ def _load():
     for f in ("gemm_bf16", "gemm_bf16_strided_batched", "gemm_bf16_variant",
               "gemm_bf16_validate", "gemm_bf16_plan", "gemm_bf16_version", "gemm_bf16_layout",
               "gemm_bf16_layout_validate", "gemm_bf16_layout_plan", "gemm_bf16_splitk",
-              "gemm_bf16_splitk_noalloc",
+              "gemm_bf16_splitk_noalloc", "gemm_bf16_streamk", "gemm_bf16_streamk_plan",
               "gemm_bf16_splitk_plan"):
         getattr(lib, f).restype = _int
     lib.gemm_bf16_kernel_name.argtypes = [_int]
@@ -256,6 +264,23 @@ def gemm_bf16_splitk_noalloc(a_layout, b_layout, splits, batch, M, N, K, A, lda,
     _check(_load().gemm_bf16_splitk_noalloc(a_layout, b_layout, splits, batch, M, N, K, _ptr(A), lda,
                                             strideA, _ptr(B), ldb, strideB, _ptr(C), ldc, strideC,
                                             out_dtype, _stream(stream)), "gemm_bf16_splitk_noalloc")
+
+
+def gemm_bf16_streamk(mode, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                      out_dtype, workspace, workspace_bytes, stream=None):
+    _check(_load().gemm_bf16_streamk(mode, batch, M, N, K, _ptr(A), lda, strideA, _ptr(B), ldb, strideB,
+                                     _ptr(C), ldc, strideC, out_dtype, _ptr(workspace), workspace_bytes,
+                                     _stream(stream)), "gemm_bf16_streamk")
+
+
+def gemm_bf16_streamk_plan(mode, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                           out_dtype, num_cus=0):
+    """(status, workspace bytes, whole tiles, cut tiles, stream-K slots, workgroups)."""
+    ws, dp, sk, sl, gx = _i64(0), _int(0), _int(0), _int(0), _i64(0)
+    rc = _load().gemm_bf16_streamk_plan(mode, batch, M, N, K, _ptr(A), lda, strideA, _ptr(B), ldb, strideB,
+                                        _ptr(C), ldc, strideC, out_dtype, num_cus, ctypes.byref(ws),
+                                        ctypes.byref(dp), ctypes.byref(sk), ctypes.byref(sl), ctypes.byref(gx))
+    return rc, ws.value, dp.value, sk.value, sl.value, gx.value
 
 
 def gemm_bf16_splitk_plan(a_layout, b_layout, splits, batch, M, N, K, A, lda, strideA, B, ldb,

@@ -120,11 +120,18 @@ __device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t r, void* lds_
 // the bijection below gives XCD x a contiguous range of logical tiles, which are then
 // rastered in groups of `group_m` tile rows so that the A and B panels they share stay in
 // that XCD's L2.
-__device__ __forceinline__ void tile_of(int t, const TileGrid& g, int& batch, int& tm, int& tn) {
+// The XCD part of that order on n items: index t (on XCD t % 8) -> logical index, XCD x taking
+// a contiguous range.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_order(int t, int n) {
     constexpr int XCD = 8;
-    int per = g.total / XCD, extra = g.total % XCD;
-    int x = t % XCD, local = t / XCD;
-    int L = (x < extra) ? x * (per + 1) + local : extra * (per + 1) + (x - extra) * per + local;
+    const int per = n / XCD, extra = n % XCD;
+    const int x = t % XCD, local = t / XCD;
+    return (x < extra) ? x * (per + 1) + local : extra * (per + 1) + (x - extra) * per + local;
+}
+
+// The raster part: logical index L -> (batch item, tile row, tile column), tile rows taken in
+// groups of group_m.
+__device__ __forceinline__ void raster_of(int L, const TileGrid& g, int& batch, int& tm, int& tn) {
     int tiles = g.tiles_m * g.tiles_n;
     batch = L / tiles;
     int r = L - batch * tiles;
@@ -134,6 +141,10 @@ __device__ __forceinline__ void tile_of(int t, const TileGrid& g, int& batch, in
     int within = r % group;
     tm = first_m + within % gm;
     tn = within / gm;
+}
+
+__device__ __forceinline__ void tile_of(int t, const TileGrid& g, int& batch, int& tm, int& tn) {
+    raster_of(xcd_order(t, g.total), g, batch, tm, tn);
 }
 
 __device__ __forceinline__ int wave_id() {
@@ -233,6 +244,33 @@ __device__ __forceinline__ void store_acc(void* Cp, int64_t ldc, int64_t M, int6
 }  // namespace tmm
 
 namespace tmm {
+
+// One fragment row of store_acc: the four consecutive outputs (m, n .. n + 3) of one lane.
+// `full`: the whole fragment lies inside M x N and C takes vector stores.
+template <int OUT>
+__device__ __forceinline__ void store_frag(void* Cp, int64_t ldc, int64_t M, int64_t N, int64_t m, int64_t n,
+                                           f32x4 v, bool full) {
+    if constexpr (OUT == OUT_F32) {
+        float* row = static_cast<float*>(Cp) + m * ldc;
+        if (full) {
+            *reinterpret_cast<f32x4*>(row + n) = v;
+        } else if (m < M) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N) row[n + r] = v[r];
+        }
+    } else {
+        uint16_t* row = static_cast<uint16_t*>(Cp) + m * ldc;
+        const u32x2 p = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        if (full) {
+            *reinterpret_cast<u32x2*>(row + n) = p;
+        } else if (m < M) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N) row[n + r] = static_cast<uint16_t>(p[r >> 1] >> (16 * (r & 1)));
+        }
+    }
+}
 
 // As store_acc, for v_mfma_f32_32x32x16_bf16 accumulators: fragment [fi][fj] holds
 // D[n][m] = C[m][n] for a 32 (n) x 32 (m) block; lane l, register r carries

@@ -14,7 +14,7 @@ using namespace tmm;
 
 namespace {
 
-constexpr int kVersion = 9;
+constexpr int kVersion = 10;
 constexpr int kDefaultCUs = 256;        // MI355X
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t k2G = int64_t(1) << 31;
@@ -451,6 +451,81 @@ int run_splitk_noalloc(const Shape& s, int splits, void* stream) {
     return run_splitk(s, splits, ws, GEMM_SCRATCH_BYTES, stream);
 }
 
+// --- stream-K with atomic work claiming ---------------------------------------------------
+struct SkPlan {
+    int T_dp = 0, T_sk = 0, G_sk = 0, grid = 0, L = 1;
+    int64_t ctr_ints = 0, part_bytes = 0, ws_bytes = 0;
+};
+
+constexpr int kSkMinBlocks = 4;            // K blocks per stream-K slot, at least
+// The counters sit in the first kSkCtrBytes of the workspace whatever the call, and the partials
+// after them, so that no call's partials land on another call's counters.
+constexpr int64_t kSkCtrBytes = 16384;
+constexpr int64_t kSkMaxIters = 1 << 22;   // stream-K iterations (the slot arithmetic's range)
+
+// Work of gemm_bf16_streamk on `cus` compute units: 256 x 256 tiles of the 4-wave ring kernel;
+// the last T_sk tiles as stream-K slots, the others whole (see gemm_ring.hip).
+int plan_streamk(int mode, const Shape& s, int cus, SkPlan& sp, Plan& p) {
+    if (mode < GEMM_STREAMK_AUTO || mode > GEMM_STREAMK_ALL) return GEMM_ERR_ARG;
+    if (s.la != GEMM_LAYOUT_K_MAJOR || s.lb != GEMM_LAYOUT_K_MAJOR || !ring_layout_ok(s)) return GEMM_ERR_UNSUPPORTED;
+    int rc = plan_spec(s, cus, p, K_RING4_256);
+    if (rc != GEMM_OK) return rc;
+    const int64_t T = p.grid.total, nk = cdiv(s.K, 64);
+    int64_t T_sk = 0;
+    if (mode != GEMM_STREAMK_DP) {
+        // the last partly filled wave together with the full wave before it (so that every
+        // slot holds more than one tile's K blocks and each cut tile has few pieces)
+        if (T > cus && T % cus != 0) T_sk = cus + T % cus;
+        else if (T < cus && mode == GEMM_STREAMK_ALL) T_sk = T;      // every tile
+    }
+    if (T_sk * nk >= kSkMaxIters) T_sk = 0;
+    sp = SkPlan{};
+    sp.T_sk = static_cast<int>(T_sk);
+    sp.T_dp = static_cast<int>(T - T_sk);
+    if (T_sk > 0) {
+        const int64_t I = T_sk * nk;
+        const int64_t G = std::min<int64_t>(cus, std::max<int64_t>(1, I / kSkMinBlocks));
+        const int64_t L = cdiv(I, G);
+        sp.L = static_cast<int>(L);
+        sp.G_sk = static_cast<int>(cdiv(I, L));   // every slot starts below I
+    }
+    const int64_t units = sp.T_dp + sp.G_sk;
+    sp.grid = static_cast<int>(std::min<int64_t>(units, cus));
+    sp.ctr_ints = 2 + sp.grid + 4 * T_sk;   // T_sk < 2 cus
+    if (sp.ctr_ints * 4 > kSkCtrBytes) return GEMM_ERR_UNSUPPORTED;   // beyond 800 compute units
+    sp.part_bytes = int64_t(sp.G_sk) * 2 * 256 * 256 * 4;
+    sp.ws_bytes = kSkCtrBytes + sp.part_bytes;
+    p.grid_x = sp.grid;
+    return GEMM_OK;
+}
+
+int run_streamk(int mode, const Shape& s, void* ws, int64_t ws_bytes, void* stream) {
+    int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
+                      s.out);
+    if (rc != GEMM_OK) return rc;
+    if (mode < GEMM_STREAMK_AUTO || mode > GEMM_STREAMK_ALL || ws_bytes < 0) return GEMM_ERR_ARG;
+    if (s.batch == 0 || s.M == 0 || s.N == 0) return GEMM_OK;
+    if (s.K == 0) return run(GEMM_VARIANT_AUTO, s, stream);
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != GEMM_OK) return rc;
+    Plan p;
+    SkPlan sp;
+    rc = plan_streamk(mode, s, cus, sp, p);
+    if (rc != GEMM_OK) return rc;
+    if (ws == nullptr) return GEMM_ERR_NULL;
+    if (!aligned(ws, 256) || ws_bytes < sp.ws_bytes) return GEMM_ERR_ARG;
+    GemmArgs g{s.batch, s.M, s.N, s.K,
+               static_cast<const uint16_t*>(s.A), s.lda, s.sA,
+               static_cast<const uint16_t*>(s.B), s.ldb, s.sB,
+               const_cast<void*>(s.C), s.ldc, s.sC, s.la, s.lb};
+    int* ctr = static_cast<int*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + kSkCtrBytes);
+    hipError_t e = launch_ring_streamk(g, s.out, p, ctr, part, sp.T_dp, sp.T_sk, sp.G_sk, sp.L,
+                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 Shape shape(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t sA,
             const void* B, int64_t ldb, int64_t sB, const void* C, int64_t ldc, int64_t sC, int out,
             int la = GEMM_LAYOUT_K_MAJOR, int lb = GEMM_LAYOUT_K_MAJOR) {
@@ -735,6 +810,38 @@ int gemm_bf16_splitk_noalloc(int a_layout, int b_layout, int splits, int64_t bat
     return run_splitk_noalloc(
         shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype, a_layout, b_layout),
         splits, stream);
+}
+
+int gemm_bf16_streamk(int mode, int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                      int64_t strideA, const void* B, int64_t ldb, int64_t strideB, void* C, int64_t ldc,
+                      int64_t strideC, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+    return run_streamk(mode, shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype),
+                       workspace, workspace_bytes, stream);
+}
+
+int gemm_bf16_streamk_plan(int mode, int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                           int64_t strideA, const void* B, int64_t ldb, int64_t strideB, const void* C,
+                           int64_t ldc, int64_t strideC, int out_dtype, int num_cus, int64_t* workspace_bytes,
+                           int* dp_tiles, int* sk_tiles, int* sk_slots, int64_t* grid_x) {
+    const Shape s = shape(batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_dtype);
+    int rc = validate(s.la, s.lb, s.batch, s.M, s.N, s.K, s.A, s.lda, s.sA, s.B, s.ldb, s.sB, s.C, s.ldc, s.sC,
+                      s.out);
+    if (rc != GEMM_OK) return rc;
+    if (mode < GEMM_STREAMK_AUTO || mode > GEMM_STREAMK_ALL) return GEMM_ERR_ARG;
+    SkPlan sp;
+    if (s.batch == 0 || s.M == 0 || s.N == 0 || s.K == 0) {
+        sp = SkPlan{};
+    } else {
+        Plan p;
+        rc = plan_streamk(mode, s, num_cus > 0 ? num_cus : kDefaultCUs, sp, p);
+        if (rc != GEMM_OK) return rc;
+    }
+    if (workspace_bytes) *workspace_bytes = sp.ws_bytes;
+    if (dp_tiles) *dp_tiles = sp.T_dp;
+    if (sk_tiles) *sk_tiles = sp.T_sk;
+    if (sk_slots) *sk_slots = sp.G_sk;
+    if (grid_x) *grid_x = sp.grid;
+    return GEMM_OK;
 }
 
 int gemm_bf16_splitk_plan(int a_layout, int b_layout, int splits, int64_t batch, int64_t M, int64_t N,

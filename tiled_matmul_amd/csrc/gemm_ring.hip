@@ -77,9 +77,86 @@ __device__ __forceinline__ int swz(int r) { return r & 7; }
 // range per tile as a compile-time constant and their registers).
 constexpr int OUT_PARTIAL = 2;
 
-template <int OUT, bool RAGGED, int WAVES_M, int WAVES_N, bool ASM, int MF, bool AMN, bool BMN>
+// Stream-K with atomic work claiming (gemm_bf16_streamk).  Work units: units 0 .. T_dp - 1 are
+// whole tiles (data-parallel); units T_dp .. T_dp + G_sk - 1 are stream-K slots: slot s is the
+// iterations [s L, min((s + 1) L, I)) of the I = T_sk * nk (tile, K block) iterations of the
+// last T_sk tiles, taken tile by tile, with L = ceil(I / G): its segments are the pieces of
+// the tiles it touches; only its first and last can be parts of a tile (any between are whole
+// tiles).  Workgroup g starts with unit g and claims each further unit with
+// an atomic add on ctr[0] (returning gridDim.x + old); the claim is made by one lane after the
+// first barrier of a unit and handed to the other waves through ctr[2 + g], read after the
+// unit's last barrier (so no wave reads a claim that is not yet made or already replaced).  A
+// tile split over several slots is finished by whichever of its segments arrives last, per
+// wave (each wave owns a 128 x 128 quarter): every such segment stores its fp32 partial quarter
+// to part[(2 s + (0 for the slot's first segment, 1 for its last)) * 4 + wave] in register
+// order (part: SK_PART_OFFSET bytes after ctr), releases it and counts itself on
+// ctr[2 + gridDim.x + 4 u + wave]; the segment that counts last acquires the others and adds
+// all partials in slot order (a fixed order, so the result does not depend on which workgroup
+// arrives last), writes C and resets the counter.  ctr[1] counts exiting workgroups; each
+// clears its ctr[2 + g] on the way out and the last one resets ctr[0] and ctr[1], so every word
+// of the counter region is zero again after the call.  No workgroup ever waits for another.
+// Only what cannot be derived is passed (the kernel keeps these live across its K loop): the
+// counters (the partials follow them at SK_PART_OFFSET bytes), the whole tiles, the cut tiles
+// and the slot length L.
+struct SkArgs {
+    int* ctr;
+    int T_dp, T_sk, L;
+};
+constexpr int SK_PART_OFFSET = 16384;
+// Cache policy of the partials' stores and loads: sc0 | sc1, system coherence (memory, not a
+// cache of one XCD).
+constexpr int SK_COHERENT = 1 | 16;
+
+// x / d for x < 2^22 and d >= 1: the float estimate (reciprocal within an ulp or two) is within
+// one of the quotient, then corrected.
+__device__ __forceinline__ uint32_t sk_div(uint32_t x, uint32_t d) {
+    uint32_t q = static_cast<uint32_t>(static_cast<float>(x) * __builtin_amdgcn_rcpf(static_cast<float>(d)));
+    if (q * d > x) --q;
+    else if ((q + 1) * d <= x) ++q;
+    return q;
+}
+
+struct SkSeg {
+    int t, kb0, nk;     // tile, first K block, K blocks
+    int u, s, part;     // stream-K tile (t - T_dp), slot, partial of the slot (0: its first segment, 1: its last)
+    int s_lo, s_hi;     // the slots that hold this tile's segments
+    bool direct;        // the whole tile: write C
+    bool has_next;      // the slot continues into the next tile
+};
+
+__device__ __forceinline__ SkSeg sk_segment(const SkArgs& a, int unit, int seg, uint32_t nk) {
+    SkSeg r{};
+    if (unit < a.T_dp) {
+        r.t = unit, r.kb0 = 0, r.nk = static_cast<int>(nk), r.direct = true, r.has_next = false;
+        return r;
+    }
+    const uint32_t L = static_cast<uint32_t>(a.L);
+    const uint32_t I = static_cast<uint32_t>(a.T_sk) * nk;
+    // slots in XCD order (the workgroups one XCD starts with take neighbouring slots)
+    const int G_sk = static_cast<int>((I + L - 1) / L);
+    const uint32_t s = static_cast<uint32_t>(xcd_order(unit - a.T_dp, G_sk));
+    const uint32_t lo = s * L, hi = min(lo + L, I);
+    const uint32_t u = sk_div(lo, nk) + static_cast<uint32_t>(seg);
+    const uint32_t tb = u * nk;
+    const uint32_t a0 = max(lo, tb), a1 = min(hi, tb + nk);
+    r.t = a.T_dp + static_cast<int>(u), r.u = static_cast<int>(u), r.s = static_cast<int>(s), r.part = seg > 0;
+    r.kb0 = static_cast<int>(a0 - tb), r.nk = static_cast<int>(a1 - a0);
+    r.has_next = hi > tb + nk;
+    r.s_lo = static_cast<int>(sk_div(tb, L));
+    r.s_hi = static_cast<int>(sk_div(tb + nk - 1, L));
+    // The divisions run on the vector unit; the results are the same in every lane, and saying
+    // so keeps the branches on them uniform (and the loop's bookkeeping in scalar registers).
+    r.t = __builtin_amdgcn_readfirstlane(r.t), r.u = __builtin_amdgcn_readfirstlane(r.u);
+    r.kb0 = __builtin_amdgcn_readfirstlane(r.kb0), r.nk = __builtin_amdgcn_readfirstlane(r.nk);
+    r.s_lo = __builtin_amdgcn_readfirstlane(r.s_lo), r.s_hi = __builtin_amdgcn_readfirstlane(r.s_hi);
+    r.has_next = __builtin_amdgcn_readfirstlane(r.has_next ? 1 : 0) != 0;
+    r.direct = r.s_lo == r.s_hi;
+    return r;
+}
+
+template <int OUT, bool RAGGED, int WAVES_M, int WAVES_N, bool ASM, int MF, bool AMN, bool BMN, bool SK = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void gemm_ring_kernel(
-    GemmArgs g, TileGrid tg, int vec_store) {
+    GemmArgs g, TileGrid tg, int vec_store, SkArgs sk) {
     using namespace rg;
     using MM = std::conditional_t<MF == 16, std::conditional_t<ASM, MmaAsm16, Mma<16>>,
                                   std::conditional_t<ASM, MmaAsm32, Mma<32>>>;
@@ -105,17 +182,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
 
     // K-major tiles.  Load i of wave w: tile rows (NW i + w) R + lane / 8; the lane writes
     // physical chunk lane % 8, i.e. fetches logical chunk (lane % 8) ^ swz(row).  R = 8, so
-    // swz(row) = lane / 8 for every i.
-    const int lrow = lane / 8;
-    const uint32_t chunk_k = 8u * static_cast<uint32_t>((lane % 8) ^ swz(lrow));
-    // Fragment reads of sub-step h of k step kk: row lane % MF of an MF-row block, logical
-    // chunk 4 kk + CPM h + lane / MF.
-    int rd[2][KH];
+    // swz(row) = lane / 8 for every i.  Fragment reads of sub-step h of k step kk: row
+    // lane % MF of an MF-row block, logical chunk 4 kk + CPM h + lane / MF.
+    auto lane_consts = [&](int ln, int& lrow_, uint32_t& chunk_k_, int (&rd_)[2][KH]) {
+        lrow_ = ln / 8;
+        chunk_k_ = 8u * static_cast<uint32_t>((ln % 8) ^ swz(lrow_));
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int h = 0; h < KH; ++h)
-            rd[kk][h] = (lane % MF) * ROWB + (((4 * kk + CPM * h + lane / MF) ^ swz(lane % MF)) * 16);
+            for (int h = 0; h < KH; ++h)
+                rd_[kk][h] = (ln % MF) * ROWB + (((4 * kk + CPM * h + ln / MF) ^ swz(ln % MF)) * 16);
+    };
+    int lrow0, rd0[2][KH];
+    uint32_t chunk_k0;
+    lane_consts(lane, lrow0, chunk_k0, rd0);
     const int a_off = wm * WM * ROWB, b_off = wn * WN * ROWB;
 
     // MN-major tiles.  Load i of wave w: k-rows (NW i + w) 2 + lane / 32, physical chunk
@@ -140,13 +220,45 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     }
     const int a_col0 = wm * WM, b_col0 = wn * WN;   // first fragment column of this wave
 
-    for (int item = blockIdx.x; item < tg.total * S; item += gridDim.x) {
+    static_assert(!SK || (OUT != OUT_PARTIAL && WAVES_M == 2 && WAVES_N == 2 && MF == 16), "stream-K layout");
+    int unit = blockIdx.x, seg = 0;   // stream-K: the current unit and segment
+    // stream-K units: the whole tiles and ceil(I / L) slots
+    const int sk_units = SK ? sk.T_dp + static_cast<int>((static_cast<uint32_t>(sk.T_sk) * nk_all + sk.L - 1) /
+                                                         static_cast<uint32_t>(sk.L))
+                            : 0;
+    for (int item = blockIdx.x; SK ? unit < sk_units : item < tg.total * S; item += gridDim.x) {
         // Work item = (tile, K range); range s covers blocks [s nk / S, (s + 1) nk / S).
-        const int t = item / S, s_rng = item - (item / S) * S;
-        const int kb0 = static_cast<int>(static_cast<int64_t>(s_rng) * nk_all / S);
-        const int nk = static_cast<int>(static_cast<int64_t>(s_rng + 1) * nk_all / S) - kb0;
+        int t = item / S, s_rng = item - (item / S) * S;
+        int kb0 = static_cast<int>(static_cast<int64_t>(s_rng) * nk_all / S);
+        int nk = static_cast<int>(static_cast<int64_t>(s_rng + 1) * nk_all / S) - kb0;
+        if constexpr (SK) {
+            const SkSeg sg = sk_segment(sk, unit, seg, static_cast<uint32_t>(nk_all));
+            t = sg.t, kb0 = sg.kb0, nk = sg.nk, s_rng = 0;
+        }
+        // The per-lane constants.  Stream-K recomputes them per work item from an opaque copy of
+        // the lane id, so that the compiler does not keep them live across the work loop, where
+        // the longer epilogue needs the registers.
+        int lrow = lrow0, rd[2][KH];
+        uint32_t chunk_k = chunk_k0;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int h = 0; h < KH; ++h) rd[kk][h] = rd0[kk][h];
+        if constexpr (SK) {
+            int lane_k = lane;
+            asm volatile("" : "+v"(lane_k));
+            lane_consts(lane_k, lrow, chunk_k, rd);
+        }
+
         int bt, tm, tn;
-        tile_of(t, tg, bt, tm, tn);
+        if constexpr (SK) {
+            // whole tiles: the XCD order over the first T_dp tiles of the raster; cut tiles: the
+            // rest of the raster, in order
+            if (t < sk.T_dp) raster_of(xcd_order(t, sk.T_dp), tg, bt, tm, tn);
+            else raster_of(t, tg, bt, tm, tn);
+        } else {
+            tile_of(t, tg, bt, tm, tn);
+        }
         const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
         const int64_t rows_a = min<int64_t>(BM, g.M - m0), rows_b = min<int64_t>(BN, g.N - n0);
         const uint16_t* Ab = g.A + bt * g.sA + (AMN ? m0 : m0 * g.lda);
@@ -252,6 +364,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         }
         wait_vmcnt<2 * L>();
         barrier();
+        if constexpr (SK) {
+            // Claim the unit after this one.  Past this barrier every wave has read the previous
+            // claim (at the end of the previous unit), so its slot can be overwritten.
+            if (seg == 0 && w == 0 && lane == 0) {
+                const int next = static_cast<int>(gridDim.x) +
+                                 __hip_atomic_fetch_add(sk.ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sk.ctr + 2 + blockIdx.x, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
         F f[2];
 #pragma unroll
         for (int q = 0; q < NR; ++q) read_one(f[0], q, 0, B_BASE, 0);
@@ -277,7 +398,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         wait_vmcnt<0>();   // the trailing zero-fill loads have landed
         barrier();         // every fragment read of this tile is done: the rings are free
 
-        if (RAGGED && s_rng == S - 1) {   // the last range holds the end of K (uniform branch)
+        // the last range (stream-K: the segment that ends the tile) holds the end of K
+        if (RAGGED && (SK ? kb0 + nk == nk_all : s_rng == S - 1)) {
             // Elements K8 .. K - 1 of every row, element by element (nothing at or beyond K is
             // read), as the first 8 k of one more 32-deep step (A in A slot 0, B in B slot 0),
             // each tile in its own layout; the rest of the step is zero.
@@ -331,7 +453,78 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         }
         if constexpr (ASM) agpr_fence(acc);
 
-        if constexpr (OUT == OUT_PARTIAL) {   // range s_rng's partial (pitch N; 16-byte stores when N % 4 == 0)
+        if constexpr (SK) {
+            const SkSeg sg = sk_segment(sk, unit, seg, static_cast<uint32_t>(nk_all));   // again: fewer live registers
+            void* const part = reinterpret_cast<char*>(sk.ctr) + SK_PART_OFFSET;
+            if (!sg.direct) {
+                // This wave's quarter of the segment's partial, in register order, written
+                // through to memory (system-coherent stores bypass the caches, so no cache
+                // maintenance is needed for another XCD to read them; a release fence would
+                // write back this XCD's whole L2).
+                const uint32_t quarter = (2u * sg.s + sg.part) * 4u + w;   // 64 KB each
+                // the workspace's partials: ceil(T_sk nk / L) slots x 2 segments x 4 quarters x 64 KB
+                const uint32_t n_slots = (static_cast<uint32_t>(sk.T_sk) * nk_all + sk.L - 1) / sk.L;
+                const auto rp = make_rsrc(part, n_slots * (2u * 4u * 65536u));
+#pragma unroll
+                for (int f = 0; f < FN * FM; ++f) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[f / FM][f % FM]), rp,
+                                                           (quarter * (FN * FM) + f) * 1024u + 16u * lane, 0,
+                                                           SK_COHERENT);
+                    if (f % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+                }
+                wait_vmcnt<0>();   // the partial is in memory before it is counted
+                int* cnt = sk.ctr + 2 + gridDim.x + 4 * sg.u + w;
+                int old = 0;
+                if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                old = __builtin_amdgcn_readfirstlane(old);
+                if (old == sg.s_hi - sg.s_lo) {   // the last segment of this tile to arrive
+                    // every segment's partial quarter, this one's included, summed in slot order
+                    const uint32_t tb = static_cast<uint32_t>(sg.u) * static_cast<uint32_t>(nk_all);
+                    void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
+                                              : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
+                    const bool full = vec_store != 0 && m0 + wm * WM + WM <= g.M && n0 + wn * WN + WN <= g.N;
+                    // 8 fragments at a time: each slot's 8 loads in flight together
+                    constexpr int FG = 8;
+#pragma unroll 1
+                    for (int f0 = 0; f0 < FN * FM; f0 += FG) {
+                        f32x4 v[FG];
+#pragma unroll 1
+                        for (int s2 = sg.s_lo; s2 <= sg.s_hi; ++s2) {
+                            // the slot's first segment if it starts in this tile, else its last
+                            const uint32_t p2 = static_cast<uint32_t>(s2) * static_cast<uint32_t>(sk.L) >= tb ? 0u : 1u;
+                            const uint32_t q2 = (2u * s2 + p2) * 4u + w;
+                            f32x4 x[FG];
+#pragma unroll
+                            for (int i = 0; i < FG; ++i)
+                                x[i] = __builtin_bit_cast(
+                                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rp, (q2 * (FN * FM) + f0 + i) * 1024u + 16u * lane, 0, SK_COHERENT));
+#pragma unroll
+                            for (int i = 0; i < FG; ++i) v[i] = s2 == sg.s_lo ? x[i] : v[i] + x[i];
+                        }
+#pragma unroll
+                        for (int i = 0; i < FG; ++i) {
+                            const int fi = (f0 + i) / FM, fj = (f0 + i) % FM;
+                            store_frag<OUT>(Cb, g.ldc, g.M, g.N, m0 + wm * WM + 16 * fj + (lane & 15),
+                                            n0 + wn * WN + 16 * fi + 4 * (lane >> 4), v[i], full);
+                        }
+                    }
+                    if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            if (sg.direct) {
+                void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
+                                          : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
+                store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
+            }
+            // Next: the slot's second segment, or the unit claimed at the start of this one
+            // (written before its barriers).  Selects rather than branches keep unit and seg in
+            // scalar registers.
+            const int claimed = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(sk.ctr + 2 + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            unit = sg.has_next ? unit : claimed;
+            seg = sg.has_next ? seg + 1 : 0;
+        } else if constexpr (OUT == OUT_PARTIAL) {   // range s_rng's partial (pitch N; 16-byte stores when N % 4 == 0)
             float* P = g.ws + (static_cast<int64_t>(s_rng) * g.batch + bt) * g.M * g.N;
             if constexpr (MF == 16)
                 store_acc<OUT_F32, FN, FM>(P, g.N, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, g.N % 4 == 0);
@@ -344,6 +537,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
                 store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
             else
                 store_acc32<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
+        }
+    }
+    if constexpr (SK) {
+        // Every wave has read this workgroup's last claim (at the end of its last unit): clear
+        // it, then count the workgroup out; the last one to leave resets the claim and exit
+        // counters.  So every word of the counter region is zero again when the call ends,
+        // whatever the layout of the next call on the same workspace.
+        barrier();
+        if (w == 0 && lane == 0) {
+            __hip_atomic_store(sk.ctr + 2 + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int e = __hip_atomic_fetch_add(sk.ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (e == static_cast<int>(gridDim.x) - 1) {
+                __hip_atomic_store(sk.ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sk.ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 }
@@ -436,22 +644,22 @@ static hipError_t launch_ring_lay(const GemmArgs& g, int out, const Plan& p, hip
     const dim3 grid(p.grid_x), block(64 * WM * WN);
     if (g.splits > 1 && ragged)
         hipLaunchKernelGGL((gemm_ring_kernel<OUT_PARTIAL, true, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g,
-                           p.grid, p.vec_store);
+                           p.grid, p.vec_store, SkArgs{});
     else if (g.splits > 1)
         hipLaunchKernelGGL((gemm_ring_kernel<OUT_PARTIAL, false, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g,
-                           p.grid, p.vec_store);
+                           p.grid, p.vec_store, SkArgs{});
     else if (out == OUT_F32 && ragged)
         hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, true, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g, p.grid,
-                           p.vec_store);
+                           p.vec_store, SkArgs{});
     else if (out == OUT_F32)
         hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, false, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g, p.grid,
-                           p.vec_store);
+                           p.vec_store, SkArgs{});
     else if (ragged)
         hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, true, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g, p.grid,
-                           p.vec_store);
+                           p.vec_store, SkArgs{});
     else
         hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, false, WM, WN, ASM, MF, AMN, BMN>), grid, block, 0, s, g, p.grid,
-                           p.vec_store);
+                           p.vec_store, SkArgs{});
     return hipGetLastError();
 }
 
@@ -475,6 +683,29 @@ static hipError_t launch_ring_cfg(const GemmArgs& g, int out, const Plan& p, hip
 #ifndef TMM_RING8_MFMA
 #define TMM_RING8_MFMA 16
 #endif
+
+// Stream-K with atomic work claiming: the 4-wave kernel, K-major operands.
+hipError_t launch_ring_streamk(const GemmArgs& g, int out, const Plan& p, int* ctr, float* part, int T_dp,
+                               int T_sk, int G_sk, int L, hipStream_t s) {
+    const bool ragged = (g.K & 7) != 0;
+    (void)G_sk;   // = ceil(T_sk nk / L), derived in the kernel
+    if (reinterpret_cast<char*>(part) != reinterpret_cast<char*>(ctr) + SK_PART_OFFSET) return hipErrorInvalidValue;
+    const SkArgs sk{ctr, T_dp, T_sk, L > 0 ? L : 1};
+    const dim3 grid(p.grid_x), block(256);
+    if (out == OUT_F32 && ragged)
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, true, 2, 2, true, 16, false, false, true>), grid, block, 0, s, g,
+                           p.grid, p.vec_store, sk);
+    else if (out == OUT_F32)
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_F32, false, 2, 2, true, 16, false, false, true>), grid, block, 0, s, g,
+                           p.grid, p.vec_store, sk);
+    else if (ragged)
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, true, 2, 2, true, 16, false, false, true>), grid, block, 0, s, g,
+                           p.grid, p.vec_store, sk);
+    else
+        hipLaunchKernelGGL((gemm_ring_kernel<OUT_BF16, false, 2, 2, true, 16, false, false, true>), grid, block, 0, s,
+                           g, p.grid, p.vec_store, sk);
+    return hipGetLastError();
+}
 
 hipError_t launch_ring(const GemmArgs& g, int out, const Plan& p, hipStream_t s) {
     switch (p.kernel) {

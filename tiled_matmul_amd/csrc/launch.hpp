@@ -49,6 +49,8 @@ hipError_t launch_mfma(const GemmArgs& g, int out, const Plan& p, hipStream_t s)
 hipError_t launch_pipe(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_pingpong(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_ring(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
+hipError_t launch_ring_streamk(const GemmArgs& g, int out, const Plan& p, int* ctr, float* part, int T_dp,
+                               int T_sk, int G_sk, int L, hipStream_t s);
 hipError_t launch_dtv(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_roles(const GemmArgs& g, int out, const Plan& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs& g, int out, hipStream_t s);

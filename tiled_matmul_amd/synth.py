@@ -196,6 +196,11 @@ WORKLOADS = {
     "ffn_down_256x4096x14336": dict(cfg=4, M=256, N=4096, K=14336, batch=1,
                                     a=("normal", (1.0,)), b=("normal", (0.02,)),
                                     out=OUT_BF16),
+    # Not one of the five: a square GEMM with 17 x 17 = 289 tiles of 256 x 256, one more than a
+    # wave of 256 compute units (with some to spare), the shape stream-K is for.  The square
+    # configuration's distributions.
+    "square_4352x4352x4096": dict(cfg=2, M=4352, N=4352, K=4096, batch=1,
+                                  a=("normal", (1.0,)), b=("normal", (1.0,)), out=OUT_FP32),
 }
 
 
