@@ -13,7 +13,9 @@ and they take ~113-128 us for a while, and only after many milliseconds settle n
 A run of 5 warm-up and 20 timed steps therefore averages across that drop; the defaults
 (300 warm-up, 5000 timed steps) time the settled state.  The amdgpu driver's clock reading is
 sampled at the start and end of the timed region and every 2 ms in between (`sclk_mhz`;
-in a region of a few milliseconds it mostly shows the clock of what ran before).  Inputs
+in a region of a few milliseconds it mostly shows the clock of what ran before, so the rate
+against the peak scaled to that clock, `roofline.frac_at_sclk`, is given only for regions of
+0.1 s or more).  Inputs
 rotate over several buffer sets whose total exceeds the 256 MB Infinity Cache, so no step
 finds its operands in a cache left warm by the previous one.  The GEMV leg captures its
 launches in a HIP graph (one kernel is a few microseconds, below the Python launch overhead)
@@ -90,6 +92,10 @@ def make_sets(name, torch, min_bytes, la=0, lb=0, pitch=None):
         b = Bd if i == 0 else Bd.clone()
         sets.append((a, b, torch.empty(cshape, dtype=out_t, device="cuda")))
     return (A, B), sets
+
+
+# Shortest timed region whose clock readings are used to scale the peak (seconds).
+SCLK_MIN_REGION_S = 0.1
 
 
 class SclkSampler:
@@ -412,8 +418,13 @@ def gemm_roofline(res):
         r = {"bound": "mfma", "achieved": res["tflops"], "peak": MFMA_TFLOPS, "unit": "TFLOP/s",
              "frac": res["tflops"] / MFMA_TFLOPS}
     if bound == "mfma" and res.get("sclk"):
-        # the same rate against the dense peak scaled to the clock the amdgpu driver reported
-        r["frac_at_sclk"] = res["tflops"] / (MFMA_TFLOPS * res["sclk"]["median"] / 2400.0)
+        # the same rate against the dense peak scaled to the clock the amdgpu driver reported;
+        # only over a region long enough for that reading to follow the clock (it trails by
+        # milliseconds, so a short region mostly reads the idle level of what ran before)
+        if (res["sclk"].get("timed_region_s") or 0.0) >= SCLK_MIN_REGION_S:
+            r["frac_at_sclk"] = res["tflops"] / (MFMA_TFLOPS * res["sclk"]["median"] / 2400.0)
+        else:
+            r["frac_at_sclk"] = None
     tr = trace_for(res["kernel"], res["name"], res["grid"], res["block"])
     if bound == "hbm":
         r["trace"] = traced_rate(tr, res["bytes"], HBM_TB_S * 1e3, 1e9)

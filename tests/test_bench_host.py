@@ -74,3 +74,15 @@ def test_traffic_taken_only_on_the_same_sources_and_launch(tmp_path, monkeypatch
     put("ring4_256", "w4", grid=256, block=256)
     put("splitk_reduce", "w4")
     assert bench.traffic_for("ring4_256+splitk_reduce", "w4", 256, 256) == 200.0   # a two-kernel call
+
+
+def test_rate_at_the_reported_clock_only_over_long_regions():
+    res = {"flops": 2.0 * 4096 ** 3, "bytes": 134217728, "tflops": 1250.0, "ms": 0.11,
+           "kernel": "ring4_256", "name": "no_such_workload", "grid": 256, "block": 256}
+    sclk = {"median": 1875, "timed_region_s": 0.5}
+    r = bench.gemm_roofline(dict(res, sclk=sclk))
+    assert abs(r["frac_at_sclk"] - 1250.0 / (2500.0 * 1875 / 2400.0)) < 1e-12
+    # a region of a few milliseconds: the reading is the idle level, no scaled rate
+    r = bench.gemm_roofline(dict(res, sclk=dict(sclk, median=462, timed_region_s=0.0022)))
+    assert r["frac_at_sclk"] is None
+    assert "frac_at_sclk" not in bench.gemm_roofline(dict(res, sclk=None))

@@ -94,3 +94,13 @@ def test_traffic_scaling_by_copy_calibration(tmp_path, monkeypatch):
     assert d["hbm_write_bytes_per_launch"] == 50.0 * 1024
     assert (d["grid"], d["block"]) == (256, 256)
     assert d["kernel_source_sha"] == pt.kernel_source_sha("ring4_256")
+
+
+def test_durations_grouped_by_launch_shape(tmp_path):
+    f = tmp_path / "k.csv"
+    hdr = "Kernel_Name,Start_Timestamp,End_Timestamp,Workgroup_Size_X,Grid_Size_X\n"
+    rows = ["k,300,1300,256,65536", "k,0,2000,256,65536", "k,100,600,1024,262144", "j,5,10,64,64"]
+    f.write_text(hdr + "\n".join(rows) + "\n")
+    d = pt.kernel_durations_by_launch(str(f))
+    # grid sizes count threads: 65536 / 256 = 256 workgroups; launch order by start time
+    assert d == {("k", 256, 256): [2000, 1000], ("k", 256, 1024): [500], ("j", 1, 64): [5]}

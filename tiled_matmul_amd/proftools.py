@@ -84,6 +84,18 @@ def kernel_durations(path):
     return {k: [dur for _, dur in sorted(v)] for k, v in d.items()}
 
 
+def kernel_durations_by_launch(path):
+    """{(kernel name, workgroups, threads per workgroup): [duration ns, ...] in launch order}
+    (the trace's grid size counts threads, so workgroups = grid size / workgroup size)."""
+    d = defaultdict(list)
+    for r in _rows(path):
+        name = r.get("Kernel_Name") or r.get("Name")
+        wg = int(r["Workgroup_Size_X"])
+        key = (name, int(r["Grid_Size_X"]) // wg, wg)
+        d[key].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return {k: [dur for _, dur in sorted(v)] for k, v in d.items()}
+
+
 def duration_quantiles(ns):
     """Average, median, min, 90th percentile (nearest rank) and max of durations in ns, in us."""
     v = sorted(ns)
@@ -167,6 +179,8 @@ def main():
     s = sub.add_parser("stats")
     s.add_argument("trace")
     s.add_argument("--skip-first", type=int, default=0)
+    s.add_argument("--by-launch", action="store_true",
+                   help="one row per kernel and launch shape (workgroups x threads)")
     t = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--workload",
               "--plan-kernel", "--out"):
@@ -201,12 +215,18 @@ def main():
                                        a.grid, a.block, a.command, a.out), indent=1))
         return
     if a.cmd == "stats":
-        print("| Kernel | Calls | Avg (us) | Median (us) | Min (us) | p90 (us) | Max (us) |")
-        print("|---|---|---|---|---|---|---|")
-        for name, v in sorted(kernel_durations(a.trace).items(), key=lambda x: -sum(x[1])):
+        if a.by_launch:
+            groups = {f"{n[:90]} | {g} x {b}": v for (n, g, b), v in kernel_durations_by_launch(a.trace).items()}
+            print("| Kernel | Launch | Calls | Avg (us) | Median (us) | Min (us) | p90 (us) | Max (us) |")
+            print("|---|---|---|---|---|---|---|---|")
+        else:
+            groups = {n[:90]: v for n, v in kernel_durations(a.trace).items()}
+            print("| Kernel | Calls | Avg (us) | Median (us) | Min (us) | p90 (us) | Max (us) |")
+            print("|---|---|---|---|---|---|---|")
+        for name, v in sorted(groups.items(), key=lambda x: -sum(x[1])):
             v = v[a.skip_first:] if len(v) > a.skip_first else v
             q = duration_quantiles(v)
-            print(f"| {name[:90]} | {len(v)} | {q['avg']:.2f} | {q['median']:.2f} | {q['min']:.2f} | "
+            print(f"| {name} | {len(v)} | {q['avg']:.2f} | {q['median']:.2f} | {q['min']:.2f} | "
                   f"{q['p90']:.2f} | {q['max']:.2f} |")
         return
     fetch, nf = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
