@@ -116,6 +116,17 @@ __device__ __forceinline__ uint32_t sk_div(uint32_t x, uint32_t d) {
     return q;
 }
 
+// Keeps the accumulators in AGPRs at this point (a register-allocation constraint only: no
+// instruction, no wait states), so that code after a branch does not have them copied out
+// before it.
+template <int FN, int FM, typename Acc>
+__device__ __forceinline__ void agpr_pin(Acc (&acc)[FN][FM]) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
 struct SkSeg {
     int t, kb0, nk;     // tile, first K block, K blocks
     int u, s, part;     // stream-K tile (t - T_dp), slot, partial of the slot (0: its first segment, 1: its last)
@@ -456,7 +467,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
         if constexpr (SK) {
             const SkSeg sg = sk_segment(sk, unit, seg, static_cast<uint32_t>(nk_all));   // again: fewer live registers
             void* const part = reinterpret_cast<char*>(sk.ctr) + SK_PART_OFFSET;
-            if (!sg.direct) {
+            if (sg.direct) {
+                // The accumulators stay in AGPRs up to the stores: without this pin the
+                // compiler copies them out before the branch for both paths, and spills.
+                agpr_pin(acc);
+                void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
+                                          : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
+                store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
+            } else {
                 // This wave's quarter of the segment's partial, in register order, written
                 // through to memory (system-coherent stores bypass the caches, so no cache
                 // maintenance is needed for another XCD to read them; a release fence would
@@ -511,11 +529,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
                     }
                     if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-            }
-            if (sg.direct) {
-                void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
-                                          : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
-                store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
             }
             // Next: the slot's second segment, or the unit claimed at the start of this one
             // (written before its barriers).  Selects rather than branches keep unit and seg in
