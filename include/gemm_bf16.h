@@ -251,10 +251,12 @@ int gemm_bf16_splitk_plan(int a_layout, int b_layout, int splits, int64_t batch,
  * atomic counter in the workspace: whole tiles first, then, for the last tiles, stream-K slots
  * of about I / G (tile, K block) iterations each (I the iterations of those tiles, G the
  * workgroups), which cut the tiles along K so that the workgroups end together.  A tile cut
- * into several pieces is summed by whichever piece finishes last, adding the fp32 partials in a
- * fixed order: the result is deterministic (bitwise the same on every run with the same
+ * into several pieces is summed by whichever piece finishes last: the others write their fp32
+ * partials to the workspace, and the last adds them and its own in a fixed order (the pieces'
+ * order along K).  The result is deterministic (bitwise the same on every run with the same
  * arguments and device), and differs from gemm_bf16 only in the order of the fp32 additions of
- * the cut tiles.
+ * the cut tiles.  No workgroup waits for one that has not started: the last piece waits only
+ * for pieces that have finished their K loop and have their stores left.
  *   mode   GEMM_STREAMK_AUTO: when there are more tiles than compute units and they do not
  *          divide evenly, stream-K for the last, partly filled wave and the full wave before it;
  *          otherwise whole tiles only.

@@ -87,14 +87,16 @@ constexpr int OUT_PARTIAL = 2;
 // first barrier of a unit and handed to the other waves through ctr[2 + g], read after the
 // unit's last barrier (so no wave reads a claim that is not yet made or already replaced).  A
 // tile split over several slots is finished by whichever of its segments arrives last, per
-// wave (each wave owns a 128 x 128 quarter): every such segment stores its fp32 partial quarter
-// to part[(2 s + (0 for the slot's first segment, 1 for its last)) * 4 + wave] in register
-// order (part: SK_PART_OFFSET bytes after ctr), releases it and counts itself on
-// ctr[2 + gridDim.x + 4 u + wave]; the segment that counts last acquires the others and adds
-// all partials in slot order (a fixed order, so the result does not depend on which workgroup
-// arrives last), writes C and resets the counter.  ctr[1] counts exiting workgroups; each
-// clears its ctr[2 + g] on the way out and the last one resets ctr[0] and ctr[1], so every word
-// of the counter region is zero again after the call.  No workgroup ever waits for another.
+// wave (each wave owns a 128 x 128 quarter), on the word ctr[2 + gridDim.x + 4 u + wave]: each
+// segment counts its arrival there (low 16 bits); every segment but the last then stores its
+// fp32 partial quarter to part[(2 s + (0 for the slot's first segment, 1 for its last)) * 4 +
+// wave] in register order (part: SK_PART_OFFSET bytes after ctr) and counts it as written
+// (high bits); the last waits for those counts, adds the partials and its own accumulators in
+// slot order (a fixed order, so the result does not depend on which workgroup arrives last),
+// writes C and resets the word.  ctr[1] counts exiting workgroups; each clears its ctr[2 + g]
+// on the way out and the last one resets ctr[0] and ctr[1], so every word of the counter
+// region is zero again after the call.  The only wait is the last segment's, for segments that
+// have arrived (they are running and have only their stores left), so it always ends.
 // Only what cannot be derived is passed (the kernel keeps these live across its K loop): the
 // counters (the partials follow them at SK_PART_OFFSET bytes), the whole tiles, the cut tiles
 // and the slot length L.
@@ -106,6 +108,9 @@ constexpr int SK_PART_OFFSET = 16384;
 // Cache policy of the partials' stores and loads: sc0 | sc1, system coherence (memory, not a
 // cache of one XCD).
 constexpr int SK_COHERENT = 1 | 16;
+// Polls of a cut tile's counter before the last piece gives up waiting (about 2^22 x 128
+// cycles, far beyond any real wait: the pieces it waits for have only their stores left).
+constexpr int kSkSpinLimit = 1 << 22;
 
 // x / d for x < 2^22 and d >= 1: the float estimate (reciprocal within an ulp or two) is within
 // one of the quotient, then corrected.
@@ -475,56 +480,83 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
                                           : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
                 store_acc<OUT, FN, FM>(Cb, g.ldc, g.M, g.N, m0 + wm * WM, n0 + wn * WN, acc, vec_store != 0);
             } else {
-                // This wave's quarter of the segment's partial, in register order, written
-                // through to memory (system-coherent stores bypass the caches, so no cache
-                // maintenance is needed for another XCD to read them; a release fence would
-                // write back this XCD's whole L2).
-                const uint32_t quarter = (2u * sg.s + sg.part) * 4u + w;   // 64 KB each
-                // the workspace's partials: ceil(T_sk nk / L) slots x 2 segments x 4 quarters x 64 KB
+                // A cut tile, per wave (each wave owns a 128 x 128 quarter).  The tile's counter
+                // word counts arrivals in its low 16 bits and written partials in its high bits.
+                // Every piece counts its arrival first.  A piece that is not the last to arrive
+                // writes its partial quarter, in register order, through to memory
+                // (system-coherent stores bypass the caches, so no cache maintenance is needed
+                // for another XCD to read them; a release fence would write back this XCD's
+                // whole L2), and then counts it as written.  The last piece to arrive writes no
+                // partial: it waits until the others' partials are counted (each of those
+                // pieces has arrived, so it is running and only has stores left: the wait ends),
+                // adds them and its own accumulators in slot order (a fixed order, so the result
+                // does not depend on which piece arrives last), writes C and clears the word.
                 const uint32_t n_slots = (static_cast<uint32_t>(sk.T_sk) * nk_all + sk.L - 1) / sk.L;
-                const auto rp = make_rsrc(part, n_slots * (2u * 4u * 65536u));
-#pragma unroll
-                for (int f = 0; f < FN * FM; ++f) {
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[f / FM][f % FM]), rp,
-                                                           (quarter * (FN * FM) + f) * 1024u + 16u * lane, 0,
-                                                           SK_COHERENT);
-                    if (f % 8 == 7) __builtin_amdgcn_sched_barrier(0);
-                }
-                wait_vmcnt<0>();   // the partial is in memory before it is counted
+                const auto rp = make_rsrc(part, n_slots * (2u * 4u * 65536u));   // slots x 2 segments x 4 quarters x 64 KB
+                const int others = sg.s_hi - sg.s_lo;   // pieces besides this one
                 int* cnt = sk.ctr + 2 + gridDim.x + 4 * sg.u + w;
                 int old = 0;
                 if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 old = __builtin_amdgcn_readfirstlane(old);
-                if (old == sg.s_hi - sg.s_lo) {   // the last segment of this tile to arrive
-                    // every segment's partial quarter, this one's included, summed in slot order
+                if ((old & 0xffff) != others) {
+                    const uint32_t quarter = (2u * sg.s + sg.part) * 4u + w;   // 64 KB each
+#pragma unroll
+                    for (int f = 0; f < FN * FM; ++f) {
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[f / FM][f % FM]), rp,
+                                                               (quarter * (FN * FM) + f) * 1024u + 16u * lane, 0,
+                                                               SK_COHERENT);
+                        if (f % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+                    }
+                    wait_vmcnt<0>();   // the partial is in memory before it is counted
+                    if (lane == 0) __hip_atomic_fetch_add(cnt, 1 << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    // Wait for the others' partials (polled with an atomic, which sees the
+                    // other XCDs' counts; bounded: past the limit the quarter is written as NaN).
+                    int v = 0;
+                    if (lane == 0) {
+                        v = __hip_atomic_fetch_add(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        for (int it = 0; (v >> 16) != others && it < kSkSpinLimit; ++it) {
+                            __builtin_amdgcn_s_sleep(2);
+                            v = __hip_atomic_fetch_add(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
+                    const bool ready = (__builtin_amdgcn_readfirstlane(v) >> 16) == others;
                     const uint32_t tb = static_cast<uint32_t>(sg.u) * static_cast<uint32_t>(nk_all);
                     void* Cb = OUT == OUT_F32 ? static_cast<void*>(static_cast<float*>(g.C) + bt * g.sC)
                                               : static_cast<void*>(static_cast<uint16_t*>(g.C) + bt * g.sC);
                     const bool full = vec_store != 0 && m0 + wm * WM + WM <= g.M && n0 + wn * WN + WN <= g.N;
                     // 8 fragments at a time: each slot's 8 loads in flight together
                     constexpr int FG = 8;
-#pragma unroll 1
+#pragma unroll
                     for (int f0 = 0; f0 < FN * FM; f0 += FG) {
-                        f32x4 v[FG];
+                        f32x4 v8[FG];
 #pragma unroll 1
                         for (int s2 = sg.s_lo; s2 <= sg.s_hi; ++s2) {
-                            // the slot's first segment if it starts in this tile, else its last
-                            const uint32_t p2 = static_cast<uint32_t>(s2) * static_cast<uint32_t>(sk.L) >= tb ? 0u : 1u;
-                            const uint32_t q2 = (2u * s2 + p2) * 4u + w;
                             f32x4 x[FG];
+                            if (s2 == sg.s) {   // this piece: its accumulators
 #pragma unroll
-                            for (int i = 0; i < FG; ++i)
-                                x[i] = __builtin_bit_cast(
-                                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rp, (q2 * (FN * FM) + f0 + i) * 1024u + 16u * lane, 0, SK_COHERENT));
+                                for (int i = 0; i < FG; ++i) x[i] = acc[(f0 + i) / FM][(f0 + i) % FM];
+                            } else {
+                                // the slot's first segment if it starts in this tile, else its last
+                                const uint32_t p2 =
+                                    static_cast<uint32_t>(s2) * static_cast<uint32_t>(sk.L) >= tb ? 0u : 1u;
+                                const uint32_t q2 = (2u * s2 + p2) * 4u + w;
 #pragma unroll
-                            for (int i = 0; i < FG; ++i) v[i] = s2 == sg.s_lo ? x[i] : v[i] + x[i];
+                                for (int i = 0; i < FG; ++i)
+                                    x[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                         rp, (q2 * (FN * FM) + f0 + i) * 1024u + 16u * lane,
+                                                                         0, SK_COHERENT));
+                            }
+#pragma unroll
+                            for (int i = 0; i < FG; ++i) v8[i] = s2 == sg.s_lo ? x[i] : v8[i] + x[i];
                         }
 #pragma unroll
                         for (int i = 0; i < FG; ++i) {
+                            if (!ready) v8[i] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                                      __builtin_nanf("")};
                             const int fi = (f0 + i) / FM, fj = (f0 + i) % FM;
                             store_frag<OUT>(Cb, g.ldc, g.M, g.N, m0 + wm * WM + 16 * fj + (lane & 15),
-                                            n0 + wn * WN + 16 * fi + 4 * (lane >> 4), v[i], full);
+                                            n0 + wn * WN + 16 * fi + 4 * (lane >> 4), v8[i], full);
                         }
                     }
                     if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
