@@ -48,7 +48,7 @@ def to_f64(C, out_dtype: int) -> np.ndarray:
 
 
 def check(C, C_ref: np.ndarray, Mag: np.ndarray, K: int, out_dtype: int) -> dict:
-    """Elementwise bound check.  Returns a summary dict; ``ok`` is the verdict."""
+    """Elementwise bound check.  Returns a summary dict; ``ok`` is the outcome."""
     Cg = to_f64(C, out_dtype)
     if Cg.shape != C_ref.shape:
         raise ValueError(f"shape mismatch {Cg.shape} vs {C_ref.shape}")

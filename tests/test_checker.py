@@ -1,6 +1,6 @@
 """The acceptance checker must reject plausible wrong results.  Each mistake is planted in
 the oracle's computation on the CPU (a dropped K tail, swapped rows, a row pitch off by one,
-truncation instead of round-to-nearest-even), then judged against the correct oracle
+truncation instead of round-to-nearest-even), then checked against the correct oracle
 result.  Integer-valued inputs make the correct result exact, so the bitwise check catches
 every mistake; the random-value bound is shown to be the looser acceptance gate.  No GPU."""
 import numpy as np
