@@ -256,7 +256,9 @@ def gemm_leg(args, torch):
         rc, ws_bytes, dp, sk, slots, grid = tm.gemm_bf16_streamk_plan(
             args.streamk, batch, M, N, K, sets[0][0], lda, sA, sets[0][1], ldb, sB, sets[0][2], N, sC, out, cus)
         block = 256
-        kname = "ring4_256"
+        # its own instances of the ring kernel: no trace or traffic summary of the static
+        # kernel applies to it
+        kname = "ring4_256 stream-K"
         sk_ws = torch.zeros(max(ws_bytes // 4, 64), dtype=torch.int32, device="cuda")
         splits = {"streamk_mode": args.streamk, "whole_tiles": dp, "cut_tiles": sk, "slots": slots}
     elif args.splits is not None:
@@ -681,7 +683,7 @@ def main():
         "roofline": gemm_roofline(res),
         "sclk_mhz": res["sclk"],
         **({"us_per_step_by_chunk": {"chunk": args.chunk, "us": res["per_chunk"]}} if args.chunk > 0 else {}),
-        "kernel_source_sha": {k: kernel_source_sha(k) for k in res["kernel"].split("+")},
+        "kernel_source_sha": {k: kernel_source_sha(k.split()[0]) for k in res["kernel"].split("+")},
     }
     if args.leg == "all" and not args.no_gemv:
         result["gemv"] = gemv_leg(args, torch)
