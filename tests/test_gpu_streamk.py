@@ -153,3 +153,26 @@ def test_streamk_errors():
         tm.gemm_bf16_streamk(tm.GEMM_STREAMK_ALL, 1, 512, 512, 512, A, 512, 0, A, 512, 0, C, 512, 0, OUT_FP32,
                              None, need)
     assert e.value.status == tm.GEMM_ERR_NULL
+
+
+def test_streamk_workload_square_4352_sampled_rows():
+    """The stream-K measurement's own workload at its full size (4352 x 4352 x 4096, 289 tiles,
+    every tile cut in the automatic mode): sampled rows (every tile row, and rows either side of
+    each tile boundary) under the bound on the workload's values, and bitwise on integers."""
+    from test_gpu_parity import sample_rows
+    name = "square_4352x4352x4096"
+    w = synth.WORKLOADS[name]
+    M, N, K, out_dtype = w["M"], w["N"], w["K"], w["out"]
+    rows = sample_rows(M)
+    A, B = synth.make_operands(name)
+    got, ws, plan = run_streamk(tm.GEMM_STREAMK_AUTO, A, B, K, out_dtype)
+    assert plan[3] == 289 and plan[2] == 0   # every tile cut
+    assert np.isfinite(got).all()
+    r = assert_bound(got[rows], A, B, K, out_dtype, rows=rows, what=name + " stream-K")
+    print(f"{name}: rows={len(rows)} max_err_over_bound={r['max_err_over_bound']:.3g}")
+    assert counters_zero(ws, plan)
+    sa, sb = synth.seeds(w["cfg"])
+    A, B = synth.integers(M, K, sa), synth.integers(N, K, sb)
+    got, ws, plan = run_streamk(tm.GEMM_STREAMK_AUTO, A, B, K, out_dtype, ws=ws)
+    assert_exact(got[rows], A, B, K, out_dtype, rows=rows, what=name + " stream-K integer")
+    assert counters_zero(ws, plan)
