@@ -256,7 +256,9 @@ int gemm_bf16_splitk_plan(int a_layout, int b_layout, int splits, int64_t batch,
  * order along K).  The result is deterministic (bitwise the same on every run with the same
  * arguments and device), and differs from gemm_bf16 only in the order of the fp32 additions of
  * the cut tiles.  No workgroup waits for one that has not started: the last piece waits only
- * for pieces that have finished their K loop and have their stores left.
+ * for pieces that have finished their K loop and have their stores left.  (That wait is bounded;
+ * past a limit no such wait reaches, the piece writes its quarter of C as NaN so that a failure
+ * shows, and the workspace's counters must then be cleared before it is used again.)
  *   mode   GEMM_STREAMK_AUTO: when there are more tiles than compute units and they do not
  *          divide evenly, stream-K for the last, partly filled wave and the full wave before it;
  *          otherwise whole tiles only.
