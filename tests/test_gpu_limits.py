@@ -73,3 +73,26 @@ def test_skinny_m_at_the_largest_pitch():
         assert_exact(out_to_host(C, m, N, N, OUT_FP32), A[:m], B, K, OUT_FP32, what=f"skinny M={m} ld {ld}")
     del dA, dB
     torch.cuda.empty_cache()
+
+
+def test_largest_batch():
+    """The largest batch the ABI accepts (65535 items; one more is an argument error), tiny
+    ragged GEMMs through gemm_bf16_strided_batched: 200 sampled items (the first and last
+    included) against the oracle bitwise, and every item finite."""
+    import torch
+    batch, M, N, K = 65535, 20, 24, 40
+    rng = np.random.default_rng(7)
+    A = rng.integers(-4, 5, size=(batch, M, K), dtype=np.int8)
+    B = rng.integers(-4, 5, size=(batch, N, K), dtype=np.int8)
+    bits = lambda x: (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # exact for small ints
+    dA = torch.from_numpy(bits(A).view(np.int16).reshape(-1)).cuda().view(torch.bfloat16)
+    dB = torch.from_numpy(bits(B).view(np.int16).reshape(-1)).cuda().view(torch.bfloat16)
+    C = empty_out(M, N, OUT_FP32, batch=batch, fill=float("nan"))
+    rc = tm.gemm_bf16_plan(0, batch + 1, M, N, K, dA, K, M * K, dB, K, N * K, C, N, M * N, OUT_FP32, 256)
+    assert rc[0] == tm.GEMM_ERR_ARG
+    tm.gemm_bf16_strided_batched(batch, M, N, K, dA, K, M * K, dB, K, N * K, C, N, M * N, OUT_FP32)
+    got = out_to_host(C, M, N, N, OUT_FP32, batch=batch)
+    assert np.isfinite(got).all()
+    items = sorted({0, batch - 1} | set(rng.integers(0, batch, 198).tolist()))
+    for b in items:
+        assert_exact(got[b], bits(A[b]), bits(B[b]), K, OUT_FP32, what=f"batch item {b}")
